@@ -1,0 +1,305 @@
+"""Plain, slow, fp64 CPU oracle for one GQA + RoPE KV-cache attention step.
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  Everything here is
+written from the mathematics the pages state; nothing is blocked, fused or
+reordered beyond what those definitions say.
+
+Pages cited (title, then section / formula / excerpt):
+  [KV]   "Llama 3.1 8B KV cache" (alijanati.com)
+  [ATL]  "Llama 3 8B - KV cache" (OpenModelAtlas, decode at position 1000)
+  [REP]  "Llama 3.1 8B - Repeat heads" (OpenModelAtlas)
+  [EP18] "Grouped-query attention: a smaller KV cache" (mvgpt, episode 18)
+  [P7]   "Part 7: The Modern Decoder Block" (openlearn course outline)
+
+Tensor conventions (all bf16 tensors are numpy uint16 bit patterns):
+  q       [B, n_q,  T, d]      new queries
+  k_new   [B, n_kv, T, d]      new keys (not yet rotated)
+  v_new   [B, n_kv, T, d]      new values
+  k_cache [B, n_kv, S, d]      rotated keys of every position so far
+  v_cache [B, n_kv, S, d]      values of every position so far
+  past_len int[B]              rows already in the cache for each sequence
+
+Parity status:
+  bf16_to_f64 / f64_to_bf16   pinned (exact bit patterns, torch RNE, ties)
+  rope_frequencies            pinned (closed form, geometric ratio)
+  llama3_scaled_frequencies   PARITY UNPINNED in the blend band: the pages name
+                              the factor and the two cutoffs but print no
+                              formula.  Only its limits are pinned (factor 1 is
+                              the identity, short wavelengths untouched,
+                              longest ones divided by the factor, continuity).
+  rotate_pairs / rope_append  pinned (complex multiplication, p = 0 identity,
+                              relative-offset invariance, index rule, sizes)
+  attend                      pinned (brute force with materialised repeat_kv
+                              and the printed mask construction, torch SDPA on
+                              CPU, closed forms, MHA/MQA special cases,
+                              prefill = prefill + decode)
+  kv_cache_bytes              pinned (every cache size the pages print)
+"""
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bf16 <-> fp64
+# ---------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits):
+    """Exact widening of bf16 bit patterns to fp64.
+
+    A bf16 number is the top half of an IEEE fp32 number, so shifting the
+    pattern into the high 16 bits of a uint32 gives the same value as fp32.
+    """
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x):
+    """Round fp64 values to bf16 directly (round to nearest, ties to even).
+
+    [ATL] (the generation excerpt) makes bf16 the default tensor type, and
+    torch's float -> bf16 cast rounds to nearest-even.  The rounding here is
+    done once, from fp64, so no double rounding through fp32 can occur.
+
+    Method: write |x| = m * 2**e with 0.5 <= m < 1 (frexp).  bf16 keeps 8
+    significant bits, so the representable numbers next to x are spaced
+    2**(e-8); below the smallest normal (2**-126) the spacing is fixed at
+    2**-133.  Scaling by a power of two is exact in fp64 and np.rint rounds
+    half to even, so y = rint(x / q) * q is the correctly rounded value.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = np.array(x, dtype=np.float64, copy=True)
+    nz = np.isfinite(x) & (x != 0.0)
+    if np.any(nz):
+        _, e = np.frexp(x[nz])
+        q = np.maximum(e - 8, -133)
+        y[nz] = np.ldexp(np.rint(np.ldexp(x[nz], -q)), q)
+    big = np.isfinite(y) & (np.abs(y) >= 2.0 ** 128)
+    y[big] = np.copysign(np.inf, y[big])
+    # y is now exactly representable in bf16, hence in fp32
+    with np.errstate(over="ignore", invalid="ignore"):
+        f32 = y.astype(np.float32)
+    u = f32.view(np.uint32)
+    nan = np.isnan(x)
+    out = (u >> np.uint32(16)).astype(np.uint16)
+    assert np.all((u[~nan] & np.uint32(0xFFFF)) == 0), "bf16 rounding left low bits set"
+    out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+
+def rope_frequencies(theta, d, scaling=None):
+    """Per-pair rotary frequencies freq_i = theta ** (-2 i / d), i = 0 .. d/2-1.
+
+    [KV] section "RoPE has to know where it is": the frequency of pair i is
+    theta raised to minus (2i / head_dim).  With ``scaling`` (a dict with
+    factor, low_freq_factor, high_freq_factor, original_max_pos) the Llama-3
+    rule below is applied afterwards ([KV] "Training details that matter"
+    names the fields; [P7] module L7.4 lists Llama-3 scaling).
+    """
+    if d % 2:
+        raise ValueError("head dimension must be even")
+    i = np.arange(d // 2, dtype=np.float64)
+    freq = np.power(float(theta), -(2.0 * i) / d)
+    if scaling is not None:
+        freq = llama3_scaled_frequencies(freq, **scaling)
+    return freq
+
+
+def llama3_scaled_frequencies(freq, factor, low_freq_factor, high_freq_factor, original_max_pos):
+    """Llama-3 frequency-dependent RoPE scaling.  PARITY UNPINNED in the blend.
+
+    Reading taken (the pages only name the fields): with wavelength
+    lambda = 2 pi / freq, wavelengths shorter than original_max_pos /
+    high_freq_factor keep their frequency, wavelengths longer than
+    original_max_pos / low_freq_factor are divided by ``factor``, and in
+    between the frequency is the mix (1 - s) freq / factor + s freq with
+    s = (original_max_pos / lambda - low_freq_factor) /
+        (high_freq_factor - low_freq_factor).
+    s is 1 at the short cutoff and 0 at the long one, so the rule is
+    continuous.
+    """
+    freq = np.asarray(freq, dtype=np.float64)
+    out = np.empty_like(freq)
+    long_cut = original_max_pos / low_freq_factor
+    short_cut = original_max_pos / high_freq_factor
+    for i, f in enumerate(freq):
+        wavelength = 2.0 * math.pi / f
+        if wavelength < short_cut:
+            out[i] = f
+        elif wavelength > long_cut:
+            out[i] = f / factor
+        else:
+            s = (original_max_pos / wavelength - low_freq_factor) / (high_freq_factor - low_freq_factor)
+            out[i] = (1.0 - s) * f / factor + s * f
+    return out
+
+
+def rotate_pairs(x, angle, layout="interleaved"):
+    """Rotate each (a, b) pair of the last axis of ``x`` by ``angle``.
+
+    [P7] key ideas: every pair of query/key dimensions turns by an angle
+    proportional to the position.  The rotation is multiplication of a + ib
+    by e^{i angle}: (a, b) -> (a cos - b sin, a sin + b cos).  Pair i uses
+    ``angle[..., i]``.  [P7] module L7.3 names two pairings:
+      interleaved: dims (2i, 2i+1)       half: dims (i, i + d/2)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    c = np.cos(angle)
+    s = np.sin(angle)
+    if layout == "interleaved":
+        a, b = x[..., 0::2], x[..., 1::2]
+    elif layout == "half":
+        a, b = x[..., : d // 2], x[..., d // 2:]
+    else:
+        raise ValueError(f"unknown RoPE layout {layout!r}")
+    ra = a * c - b * s
+    rb = a * s + b * c
+    out = np.empty(np.broadcast_shapes(x.shape, ra.shape[:-1] + (d,)), dtype=np.float64)
+    if layout == "interleaved":
+        out[..., 0::2], out[..., 1::2] = ra, rb
+    else:
+        out[..., : d // 2], out[..., d // 2:] = ra, rb
+    return out
+
+
+def rope_append(q, k_new, v_new, k_cache, v_cache, past_len, theta, layout="interleaved", scaling=None):
+    """RoPE on q and the new k at offset past_len, then write k_rot and v into the cache.
+
+    [KV] "RoPE has to know where it is": new token t of a sequence with
+    past_len cached rows sits at position past_len + t.
+    [ATL] cache formula: the call writes cache rows past_len .. past_len+T-1
+    with the rotated keys and the values; the keys are stored after rotation.
+    All other rows keep their contents.  q_rot and k_rot are rounded to bf16
+    once, from fp64; v is copied bit for bit.
+
+    Returns (q_rot, k_cache_out, v_cache_out) as new uint16 arrays.
+    """
+    q = np.asarray(q, dtype=np.uint16)
+    k_new = np.asarray(k_new, dtype=np.uint16)
+    v_new = np.asarray(v_new, dtype=np.uint16)
+    B, n_q, T, d = q.shape
+    S = k_cache.shape[2]
+    freq = rope_frequencies(theta, d, scaling)
+    q_rot = np.empty_like(q)
+    kc = np.array(k_cache, dtype=np.uint16, copy=True)
+    vc = np.array(v_cache, dtype=np.uint16, copy=True)
+    for b in range(B):
+        pos = int(past_len[b]) + np.arange(T, dtype=np.float64)
+        if int(past_len[b]) < 0 or int(past_len[b]) + T > S:
+            raise ValueError("past_len + T exceeds the cache")
+        angle = pos[:, None] * freq[None, :]  # [T, d/2]
+        q_rot[b] = f64_to_bf16(rotate_pairs(bf16_to_f64(q[b]), angle[None], layout))
+        k_rot = f64_to_bf16(rotate_pairs(bf16_to_f64(k_new[b]), angle[None], layout))
+        rows = int(past_len[b]) + np.arange(T)
+        kc[b][:, rows, :] = k_rot
+        vc[b][:, rows, :] = v_new[b]
+    return q_rot, kc, vc
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+
+def attend(q_rot, k_cache, v_cache, past_len, n_kv, scale=None):
+    """Grouped-query attention of the new queries over the cache, in fp64.
+
+    Head map ([REP] formula; [EP18] "Our six heads, three ways"): query head
+    h reads KV head floor(h / g) with g = n_q / n_kv.
+    Scores ([KV] "The cache itself is concatenation"): q . k / sqrt(d).
+    Mask ([ATL] Transformer.forward excerpt): new row t of a sequence with
+    past_len P is at position P + t and sees cache rows 0 .. P + t.
+    Softmax over the visible rows, then the weighted sum of the value rows.
+    Rows at or beyond P + T are never read.
+
+    Returns float64 [B, n_q, T, d].
+    """
+    q_rot = np.asarray(q_rot, dtype=np.uint16)
+    B, n_q, T, d = q_rot.shape
+    if n_q % n_kv:
+        raise ValueError(f"n_q={n_q} is not a multiple of n_kv={n_kv}")
+    g = n_q // n_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, n_q, T, d), dtype=np.float64)
+    t_of_row = np.tile(np.arange(T), g)  # rows of the [g*T, L] score block are (head, t)
+    for b in range(B):
+        P = int(past_len[b])
+        L = P + T
+        for j in range(n_kv):
+            K = bf16_to_f64(k_cache[b, j, :L])
+            V = bf16_to_f64(v_cache[b, j, :L])
+            Q = bf16_to_f64(q_rot[b, j * g:(j + 1) * g]).reshape(g * T, d)
+            s = (Q @ K.T) * scale
+            visible = np.arange(L)[None, :] <= (P + t_of_row)[:, None]
+            s = np.where(visible, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            w = w / w.sum(axis=1, keepdims=True)
+            out[b, j * g:(j + 1) * g] = (w @ V).reshape(g, T, d)
+    return out
+
+
+def attend_bruteforce(q_rot, k_cache, v_cache, past_len, n_kv, scale=None):
+    """Second formulation of ``attend`` for tiny shapes: explicit loops.
+
+    It follows the pages' own construction literally: the KV heads are
+    first copied out to one per query head ([REP] repeat_kv formula:
+    K_G[h] = K[floor(h / g)]), and the additive mask is built as in the [ATL]
+    Transformer.forward excerpt: zeros over the past_len cached columns next
+    to an upper-triangular -inf block (strictly above the diagonal) over the
+    new ones.  Exponentials and sums are plain Python floats.
+    """
+    q = bf16_to_f64(q_rot)
+    B, n_q, T, d = q.shape
+    g = n_q // n_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, n_q, T, d), dtype=np.float64)
+    for b in range(B):
+        P = int(past_len[b])
+        L = P + T
+        kb = bf16_to_f64(k_cache[b][:, :L])
+        vb = bf16_to_f64(v_cache[b][:, :L])
+        k_rep = [kb[h // g] for h in range(n_q)]
+        v_rep = [vb[h // g] for h in range(n_q)]
+        new_block = [[(-math.inf if col > row else 0.0) for col in range(T)] for row in range(T)]
+        mask = [[0.0] * P + new_block[row] for row in range(T)]
+        for h in range(n_q):
+            for t in range(T):
+                scores = []
+                for r in range(L):
+                    dot = 0.0
+                    for c in range(d):
+                        dot += q[b, h, t, c] * k_rep[h][r, c]
+                    scores.append(dot * scale + mask[t][r])
+                top = max(scores)
+                weights = [math.exp(x - top) for x in scores]
+                total = sum(weights)
+                for c in range(d):
+                    acc = 0.0
+                    for r in range(L):
+                        acc += weights[r] * v_rep[h][r, c]
+                    out[b, h, t, c] = acc / total
+    return out
+
+
+# ---------------------------------------------------------------------------
+# sizes
+# ---------------------------------------------------------------------------
+
+
+def kv_cache_bytes(n_layers, n_kv, head_dim, tokens, bytes_per_number):
+    """Bytes a KV cache holds: one key and one value per layer, KV head, channel and token.
+
+    [EP18] "The cache's size, and the flags": per token the cache keeps a key
+    and a value for each layer, each KV head and each channel of a head.
+    """
+    return 2 * n_layers * n_kv * head_dim * tokens * bytes_per_number

@@ -1,0 +1,147 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins catch each one.
+
+Each mutant is the oracle's source with one edit (a wrong sign, index, offset,
+operand or dropped term), loaded as a separate module on the CPU.  The pins
+below are the same independent references the oracle tests use; every
+mutant must fail at least one of them, while the unmodified source passes all.
+"""
+
+import importlib.util
+import math
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = open(os.path.join(ROOT, "oracle", "gqa_oracle.py")).read()
+
+MUTANTS = {
+    "rotation sign": ("ra = a * c - b * s", "ra = a * c + b * s"),
+    "rotation output swapped": ("rb = a * s + b * c", "rb = a * s - b * c"),
+    "half pairing": ("a, b = x[..., : d // 2], x[..., d // 2:]", "a, b = x[..., d // 2:], x[..., : d // 2]"),
+    "no position offset": ("pos = int(past_len[b]) + np.arange(T, dtype=np.float64)",
+                           "pos = np.arange(T, dtype=np.float64)"),
+    "frequency exponent": ("freq = np.power(float(theta), -(2.0 * i) / d)",
+                           "freq = np.power(float(theta), -(1.0 * i) / d)"),
+    "head map modulo": ("Q = bf16_to_f64(q_rot[b, j * g:(j + 1) * g]).reshape(g * T, d)",
+                        "Q = bf16_to_f64(q_rot[b, j::n_kv]).reshape(g * T, d)"),
+    "mask off by one": ("visible = np.arange(L)[None, :] <= (P + t_of_row)[:, None]",
+                        "visible = np.arange(L)[None, :] < (P + t_of_row)[:, None]"),
+    "mask ignores past": ("visible = np.arange(L)[None, :] <= (P + t_of_row)[:, None]",
+                          "visible = np.arange(L)[None, :] <= (t_of_row)[:, None]"),
+    "row order of score block": ("t_of_row = np.tile(np.arange(T), g)", "t_of_row = np.repeat(np.arange(T), g)"),
+    "missing scale": ("s = (Q @ K.T) * scale", "s = (Q @ K.T)"),
+    "keys not transposed": ("s = (Q @ K.T) * scale", "s = (Q @ K[:, ::-1].T) * scale"),
+    "softmax not normalised": ("w = w / w.sum(axis=1, keepdims=True)", "w = w / w.sum(axis=1, keepdims=True).max()"),
+    "value not written": ("vc[b][:, rows, :] = v_new[b]", "pass"),
+    "key written unrotated": ("kc[b][:, rows, :] = k_rot", "kc[b][:, rows, :] = k_new[b]"),
+    "ties away from zero": ("y[nz] = np.ldexp(np.rint(np.ldexp(x[nz], -q)), q)",
+                            "y[nz] = np.ldexp(np.trunc(np.ldexp(x[nz], -q) + np.copysign(0.5, x[nz])), q)"),
+}
+
+
+def load(src, name):
+    mod = types.ModuleType(name)
+    exec(compile(src, name, "exec"), mod.__dict__)
+    return mod
+
+
+def rb(rng, shape):
+    x = rng.standard_normal(shape).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---- independent pins, each returns True when the module passes it
+
+def pin_complex_rotation(m):
+    rng = np.random.default_rng(3)
+    ok = True
+    for layout in ("interleaved", "half"):
+        x = rng.standard_normal((4, 16))
+        ang = rng.uniform(-9, 9, size=(4, 8))
+        got = m.rotate_pairs(x, ang, layout)
+        lo, hi = (x[:, 0::2], x[:, 1::2]) if layout == "interleaved" else (x[:, :8], x[:, 8:])
+        z = (lo + 1j * hi) * np.exp(1j * ang)
+        glo, ghi = (got[:, 0::2], got[:, 1::2]) if layout == "interleaved" else (got[:, :8], got[:, 8:])
+        ok &= np.allclose(glo, z.real, atol=1e-12) and np.allclose(ghi, z.imag, atol=1e-12)
+    return ok
+
+
+def pin_frequencies(m):
+    f = m.rope_frequencies(1.0e4, 64)
+    return f[0] == 1.0 and np.allclose(np.diff(np.log(f)), -2 * math.log(1.0e4) / 64, atol=1e-12)
+
+
+def pin_position_offset(m):
+    rng = np.random.default_rng(4)
+    P, d = 6, 8
+    qa, ka, va = rb(rng, (1, 2, P + 1, d)), rb(rng, (1, 1, P + 1, d)), rb(rng, (1, 1, P + 1, d))
+    kc, vc = rb(rng, (1, 1, 10, d)), rb(rng, (1, 1, 10, d))
+    qall, kall, vall = m.rope_append(qa, ka, va, kc, vc, np.array([0]), 100.0)
+    qone, kone, vone = m.rope_append(qa[:, :, P:], ka[:, :, P:], va[:, :, P:], kc, vc, np.array([P]), 100.0)
+    # the unrotated key must not be what is stored (position P != 0)
+    return (np.array_equal(qone[:, :, 0], qall[:, :, P]) and np.array_equal(kone[:, :, P], kall[:, :, P])
+            and np.array_equal(vone[:, :, P], va[:, :, P]) and not np.array_equal(kone[:, :, P], ka[:, :, P]))
+
+
+def pin_torch_cast(m):
+    x32 = np.random.default_rng(5).standard_normal(4000).astype(np.float32)
+    x32 = np.concatenate([x32, np.float32([1.0 + 2 ** -8, -(1.0 + 2 ** -8), 1.0 + 3 * 2 ** -8])])
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return np.array_equal(m.f64_to_bf16(x32.astype(np.float64)), ref)
+
+
+def pin_sdpa(m):
+    rng = np.random.default_rng(6)
+    B, n_q, n_kv, T, d, past = 2, 6, 2, 3, 16, [5, 9]
+    S = 14
+    q, kc, vc = rb(rng, (B, n_q, T, d)), rb(rng, (B, n_kv, S, d)), rb(rng, (B, n_kv, S, d))
+    got = m.attend(q, kc, vc, np.array(past), n_kv)
+    g = n_q // n_kv
+    for b in range(B):
+        L = past[b] + T
+        K = torch.from_numpy(f64(kc[b][:, :L])).repeat_interleave(g, dim=0)
+        V = torch.from_numpy(f64(vc[b][:, :L])).repeat_interleave(g, dim=0)
+        allowed = torch.arange(L)[None, :] <= (past[b] + torch.arange(T))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(f64(q[b])), K, V, attn_mask=allowed)
+        if not np.allclose(got[b], ref.numpy(), atol=1e-12):
+            return False
+    return True
+
+
+def pin_bruteforce(m):
+    rng = np.random.default_rng(7)
+    q, kc, vc = rb(rng, (1, 4, 2, 4)), rb(rng, (1, 2, 6, 4)), rb(rng, (1, 2, 6, 4))
+    return np.allclose(m.attend(q, kc, vc, np.array([3]), 2), m.attend_bruteforce(q, kc, vc, np.array([3]), 2),
+                       atol=1e-12)
+
+
+PINS = [pin_complex_rotation, pin_frequencies, pin_position_offset, pin_torch_cast, pin_sdpa, pin_bruteforce]
+
+
+def test_unmodified_oracle_passes_every_pin():
+    m = load(SRC, "oracle_copy")
+    assert all(p(m) for p in PINS)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name!r} not found"
+    m = load(SRC.replace(old, new), "oracle_mutant")
+    failed = []
+    for p in PINS:
+        try:
+            if not p(m):
+                failed.append(p.__name__)
+        except Exception:
+            failed.append(p.__name__ + " (raised)")
+    assert failed, f"no pin caught mutant {name!r}"
