@@ -1,1 +1,245 @@
-"""MI355X-native grouped-query attention step with RoPE over a bf16 KV cache."""
+"""MI355X-native grouped-query attention step with RoPE over a bf16 KV cache.
+
+Thin ctypes binding over libgqa.so (``include/gqa.h``).  The functions carry
+the C ABI's names and only marshal arguments: every step of the attention
+step runs in the library's HIP kernels.  torch is used for device memory and
+the current stream, nothing else.  If libgqa.so is missing the first call
+raises: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgqa.so")
+
+GQA_OK = 0
+GQA_ERR_INVALID_ARG = -1
+GQA_ERR_GROUP = -2
+GQA_ERR_HEAD_DIM = -3
+GQA_ERR_RANGE = -4
+GQA_ERR_WORKSPACE = -5
+GQA_ERR_HIP = -6
+
+GQA_ROPE_INTERLEAVED = 0
+GQA_ROPE_HALF = 1
+
+EXPORTED = (
+    "gqa_rope_append",
+    "gqa_decode_workspace_bytes",
+    "gqa_decode_attn",
+    "gqa_prefill_attn",
+    "gqa_status_string",
+    "gqa_profile_enable",
+    "gqa_profile_read",
+    "gqa_profile_reset",
+    "gqa_set_decode_workgroups",
+)
+
+KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3}
+
+
+class GqaRopeParams(ctypes.Structure):
+    _fields_ = [
+        ("theta", ctypes.c_double),
+        ("layout", ctypes.c_int),
+        ("scaled", ctypes.c_int),
+        ("factor", ctypes.c_double),
+        ("low_freq_factor", ctypes.c_double),
+        ("high_freq_factor", ctypes.c_double),
+        ("original_max_pos", ctypes.c_double),
+    ]
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libgqa.so once; raise if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(hipcc, gfx950); there is no fallback implementation")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    L.gqa_rope_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                  ctypes.POINTER(GqaRopeParams), vp]
+    L.gqa_rope_append.restype = i32
+    L.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.gqa_decode_workspace_bytes.restype = sz
+    L.gqa_decode_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, sz, i32, i32, i32, i32, i32, f32, vp]
+    L.gqa_decode_attn.restype = i32
+    L.gqa_prefill_attn.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+    L.gqa_prefill_attn.restype = i32
+    L.gqa_status_string.argtypes = [i32]
+    L.gqa_status_string.restype = ctypes.c_char_p
+    L.gqa_profile_enable.argtypes = [i32]
+    L.gqa_profile_enable.restype = i32
+    L.gqa_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)]
+    L.gqa_profile_read.restype = i32
+    L.gqa_profile_reset.argtypes = []
+    L.gqa_profile_reset.restype = i32
+    L.gqa_set_decode_workgroups.argtypes = [i32]
+    L.gqa_set_decode_workgroups.restype = i32
+    _lib = L
+    return L
+
+
+def gqa_status_string(status):
+    return lib().gqa_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status == GQA_OK:
+        return
+    msg = gqa_status_string(status)
+    if status in (GQA_ERR_INVALID_ARG, GQA_ERR_GROUP, GQA_ERR_HEAD_DIM, GQA_ERR_RANGE, GQA_ERR_WORKSPACE):
+        raise ValueError(f"{msg} (status {status})")
+    raise GqaError(status, msg)
+
+
+# ---------------------------------------------------------------- torch marshalling helpers
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bf16(t, name, shape=None):
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _past(past_len, B):
+    import torch
+    if past_len.dtype != torch.int32 or not past_len.is_cuda or past_len.numel() != B:
+        raise ValueError("past_len must be a device int32 tensor with B entries")
+    return past_len.contiguous()
+
+
+def rope_params(theta, layout="interleaved", scaling=None):
+    p = GqaRopeParams()
+    p.theta = float(theta)
+    p.layout = {"interleaved": GQA_ROPE_INTERLEAVED, "half": GQA_ROPE_HALF}[layout]
+    p.scaled = 1 if scaling else 0
+    if scaling:
+        p.factor = float(scaling["factor"])
+        p.low_freq_factor = float(scaling["low_freq_factor"])
+        p.high_freq_factor = float(scaling["high_freq_factor"])
+        p.original_max_pos = float(scaling["original_max_pos"])
+    return p
+
+
+# ---------------------------------------------------------------- entry points
+
+def gqa_rope_append(q, k_new, v_new, k_cache, v_cache, past_len, max_past_len, theta,
+                    layout="interleaved", scaling=None, q_rot=None, stream=None):
+    """Rotate q and k_new at positions past_len[b] + t and append k_rot, v to the cache.
+
+    q [B, n_q, T, d], k_new/v_new [B, n_kv, T, d], caches [B, n_kv, S, d] (bf16, device),
+    past_len int32 [B] (device).  Returns q_rot (a new tensor unless given; may be q).
+    """
+    import torch
+    B, n_q, T, d = q.shape
+    n_kv, S = k_cache.shape[1], k_cache.shape[2]
+    _bf16(q, "q")
+    _bf16(k_new, "k_new", (B, n_kv, T, d))
+    _bf16(v_new, "v_new", (B, n_kv, T, d))
+    _bf16(k_cache, "k_cache", (B, n_kv, S, d))
+    _bf16(v_cache, "v_cache", (B, n_kv, S, d))
+    past_len = _past(past_len, B)
+    if q_rot is None:
+        q_rot = torch.empty_like(q)
+    _bf16(q_rot, "q_rot", (B, n_q, T, d))
+    p = rope_params(theta, layout, scaling)
+    _check(lib().gqa_rope_append(_ptr(q), _ptr(q_rot), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(past_len), int(max_past_len), B, n_q, n_kv, T, d, S, ctypes.byref(p),
+                                 _stream(stream)))
+    return q_rot
+
+
+def gqa_decode_workspace_bytes(B, n_q, n_kv, d, S):
+    return int(lib().gqa_decode_workspace_bytes(B, n_q, n_kv, d, S))
+
+
+def gqa_decode_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, workspace=None, scale=0.0,
+                    stream=None):
+    """One new query per sequence attends to cache rows 0..past_len[b]; returns out [B, n_q, 1, d] bf16."""
+    import torch
+    B, n_q, T, d = q_rot.shape
+    if T != 1:
+        raise ValueError("decode takes exactly one new token per sequence")
+    n_kv, S = k_cache.shape[1], k_cache.shape[2]
+    _bf16(q_rot, "q_rot")
+    _bf16(k_cache, "k_cache", (B, n_kv, S, d))
+    _bf16(v_cache, "v_cache", (B, n_kv, S, d))
+    past_len = _past(past_len, B)
+    if out is None:
+        out = torch.empty_like(q_rot)
+    _bf16(out, "out", (B, n_q, 1, d))
+    need = gqa_decode_workspace_bytes(B, n_q, n_kv, d, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_rot.device)
+    _check(lib().gqa_decode_attn(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
+                                 _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B, n_q,
+                                 n_kv, d, S, float(scale), _stream(stream)))
+    return out
+
+
+def gqa_prefill_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, scale=0.0, stream=None):
+    """T new queries per sequence under the rectangular causal mask; returns out [B, n_q, T, d] bf16."""
+    import torch
+    B, n_q, T, d = q_rot.shape
+    n_kv, S = k_cache.shape[1], k_cache.shape[2]
+    _bf16(q_rot, "q_rot")
+    _bf16(k_cache, "k_cache", (B, n_kv, S, d))
+    _bf16(v_cache, "v_cache", (B, n_kv, S, d))
+    past_len = _past(past_len, B)
+    if out is None:
+        out = torch.empty_like(q_rot)
+    _bf16(out, "out", (B, n_q, T, d))
+    _check(lib().gqa_prefill_attn(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
+                                  _ptr(out), B, n_q, n_kv, T, d, S, float(scale), _stream(stream)))
+    return out
+
+
+def gqa_profile_enable(on=True):
+    _check(lib().gqa_profile_enable(1 if on else 0))
+
+
+def gqa_profile_reset():
+    _check(lib().gqa_profile_reset())
+
+
+def gqa_profile_read(kind):
+    """(total device ms, launches) of one kernel kind since the last reset."""
+    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
+    ms = ctypes.c_double()
+    n = ctypes.c_longlong()
+    _check(lib().gqa_profile_read(k, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def gqa_set_decode_workgroups(n):
+    return int(lib().gqa_set_decode_workgroups(int(n)))

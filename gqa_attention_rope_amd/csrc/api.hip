@@ -1,0 +1,216 @@
+// C ABI of libgqa: argument validation, workspace sizing, launch, status text,
+// and the optional kernel-timing hooks.  Every check runs on the host before
+// any HIP call, so an invalid call launches nothing.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/gqa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "";
+
+int hip_status(hipError_t e) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s (%d)", hipGetErrorString(e), (int)e);
+    return GQA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks common to every entry point.
+int check_shape(int B, int n_q, int n_kv, int T, int d, int S, int max_past_len) {
+    if (B <= 0 || n_q <= 0 || n_kv <= 0 || T <= 0 || d <= 0 || S <= 0) return GQA_ERR_INVALID_ARG;
+    if (d & 1) return GQA_ERR_INVALID_ARG;
+    if (n_q % n_kv) return GQA_ERR_GROUP;
+    if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
+    if (max_past_len < 0 || (long long)max_past_len + T > (long long)S) return GQA_ERR_RANGE;
+    return GQA_OK;
+}
+
+int ensure_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    int n = 0;
+    e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return hip_status(e);
+    if (n <= 0) return hip_status(hipErrorNoDevice);
+    return GQA_OK;
+}
+
+float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+// ---- kernel timing -------------------------------------------------------------
+struct EvPair {
+    hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<EvPair> g_prof[gqa::K_KINDS];
+hipEvent_t g_pending[gqa::K_KINDS] = {};
+
+int g_decode_wg = 0;
+
+}  // namespace
+
+namespace gqa {
+
+void prof_begin(int kind, hipStream_t st) {
+    if (!g_prof_on) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, st);
+    g_pending[kind] = e;
+}
+
+void prof_end(int kind, hipStream_t st) {
+    if (!g_prof_on || !g_pending[kind]) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, st);
+    g_prof[kind].push_back(EvPair{g_pending[kind], e});
+    g_pending[kind] = nullptr;
+}
+
+}  // namespace gqa
+
+extern "C" {
+
+int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, const int32_t* past_len, int max_past_len, int B, int n_q, int n_kv, int T,
+                    int d, int S, const gqa_rope_params* rope, void* stream) {
+    if (!q || !q_rot || !k_new || !v_new || !k_cache || !v_cache || !past_len || !rope) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(q_rot) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(past_len) & 3u))
+        return GQA_ERR_INVALID_ARG;
+    if (!(rope->theta > 0.0) || !isfinite(rope->theta)) return GQA_ERR_INVALID_ARG;
+    if (rope->layout != GQA_ROPE_INTERLEAVED && rope->layout != GQA_ROPE_HALF) return GQA_ERR_INVALID_ARG;
+    if (rope->scaled != 0 && rope->scaled != 1) return GQA_ERR_INVALID_ARG;
+    if (rope->scaled) {
+        if (!(rope->factor > 0.0) || !(rope->low_freq_factor > 0.0) ||
+            !(rope->high_freq_factor > rope->low_freq_factor) || !(rope->original_max_pos > 0.0) ||
+            !isfinite(rope->factor) || !isfinite(rope->high_freq_factor) || !isfinite(rope->original_max_pos))
+            return GQA_ERR_INVALID_ARG;
+    }
+    int st = check_shape(B, n_q, n_kv, T, d, S, max_past_len);
+    if (st != GQA_OK) return st;
+    st = ensure_device();
+    if (st != GQA_OK) return st;
+    gqa::RopeDev rd;
+    rd.theta = rope->theta;
+    rd.layout = rope->layout;
+    rd.scaled = rope->scaled;
+    rd.factor = rope->scaled ? rope->factor : 1.0;
+    rd.low_freq_factor = rope->scaled ? rope->low_freq_factor : 1.0;
+    rd.high_freq_factor = rope->scaled ? rope->high_freq_factor : 2.0;
+    rd.original_max_pos = rope->scaled ? rope->original_max_pos : 1.0;
+    hipError_t e = gqa::launch_rope_append(
+        static_cast<const uint16_t*>(q), static_cast<uint16_t*>(q_rot), static_cast<const uint16_t*>(k_new),
+        static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+        past_len, max_past_len, B, n_q, n_kv, T, d, S, rd, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : hip_status(e);
+}
+
+size_t gqa_decode_workspace_bytes(int B, int n_q, int n_kv, int d, int S) {
+    if (check_shape(B, n_q, n_kv, 1, d, S, 0) != GQA_OK) return 0;
+    return gqa::decode_workspace_bytes(B, n_q, n_kv, d);
+}
+
+int gqa_decode_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                    int max_past_len, void* out, void* workspace, size_t workspace_bytes, int B, int n_q, int n_kv,
+                    int d, int S, float scale, void* stream) {
+    if (!q_rot || !k_cache || !v_cache || !past_len || !out || !workspace) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(workspace) || (reinterpret_cast<uintptr_t>(past_len) & 3u))
+        return GQA_ERR_INVALID_ARG;
+    if (!(scale == scale) || isinf(scale)) return GQA_ERR_INVALID_ARG;
+    int st = check_shape(B, n_q, n_kv, 1, d, S, max_past_len);
+    if (st != GQA_OK) return st;
+    if (workspace_bytes < gqa::decode_workspace_bytes(B, n_q, n_kv, d)) return GQA_ERR_WORKSPACE;
+    st = ensure_device();
+    if (st != GQA_OK) return st;
+    hipError_t e = gqa::launch_decode(static_cast<const uint16_t*>(q_rot), static_cast<const uint16_t*>(k_cache),
+                                      static_cast<const uint16_t*>(v_cache), past_len, max_past_len,
+                                      static_cast<uint16_t*>(out), static_cast<float*>(workspace), B, n_q, n_kv, d,
+                                      S, resolve_scale(scale, d), g_decode_wg, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : hip_status(e);
+}
+
+int gqa_prefill_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                     int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
+                     void* stream) {
+    if (!q_rot || !k_cache || !v_cache || !past_len || !out) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(past_len) & 3u))
+        return GQA_ERR_INVALID_ARG;
+    if (!(scale == scale) || isinf(scale)) return GQA_ERR_INVALID_ARG;
+    int st = check_shape(B, n_q, n_kv, T, d, S, max_past_len);
+    if (st != GQA_OK) return st;
+    if (n_kv > 65535) return GQA_ERR_INVALID_ARG;
+    st = ensure_device();
+    if (st != GQA_OK) return st;
+    hipError_t e = gqa::launch_prefill(static_cast<const uint16_t*>(q_rot), static_cast<const uint16_t*>(k_cache),
+                                       static_cast<const uint16_t*>(v_cache), past_len, max_past_len,
+                                       static_cast<uint16_t*>(out), B, n_q, n_kv, T, d, S, resolve_scale(scale, d),
+                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : hip_status(e);
+}
+
+const char* gqa_status_string(int status) {
+    switch (status) {
+        case GQA_OK: return "ok";
+        case GQA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, non-positive size, odd d, bad RoPE parameters)";
+        case GQA_ERR_GROUP: return "n_q is not a multiple of n_kv";
+        case GQA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+        case GQA_ERR_RANGE: return "max_past_len must be >= 0 and max_past_len + T <= S";
+        case GQA_ERR_WORKSPACE: return "workspace smaller than gqa_decode_workspace_bytes()";
+        case GQA_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int gqa_profile_enable(int on) {
+    g_prof_on = on != 0;
+    return GQA_OK;
+}
+
+int gqa_profile_read(int kind, double* total_ms, long long* launches) {
+    if (kind < 0 || kind >= gqa::K_KINDS || !total_ms || !launches) return GQA_ERR_INVALID_ARG;
+    double sum = 0.0;
+    for (const EvPair& p : g_prof[kind]) {
+        hipError_t e = hipEventSynchronize(p.b);
+        if (e != hipSuccess) return hip_status(e);
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, p.a, p.b);
+        if (e != hipSuccess) return hip_status(e);
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = (long long)g_prof[kind].size();
+    return GQA_OK;
+}
+
+int gqa_profile_reset(void) {
+    for (int k = 0; k < gqa::K_KINDS; ++k) {
+        for (const EvPair& p : g_prof[k]) {
+            hipEventDestroy(p.a);
+            hipEventDestroy(p.b);
+        }
+        g_prof[k].clear();
+        if (g_pending[k]) {
+            hipEventDestroy(g_pending[k]);
+            g_pending[k] = nullptr;
+        }
+    }
+    return GQA_OK;
+}
+
+int gqa_set_decode_workgroups(int n) {
+    g_decode_wg = n < 0 ? 0 : (n > gqa::DECODE_MAX_WG ? gqa::DECODE_MAX_WG : n);
+    return g_decode_wg;
+}
+
+}  // extern "C"

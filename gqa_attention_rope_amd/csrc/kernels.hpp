@@ -1,0 +1,57 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// RoPE parameters as the kernels see them (validated on the host).
+struct RopeDev {
+    double theta;
+    double factor, low_freq_factor, high_freq_factor, original_max_pos;
+    int layout;  // 0 interleaved pairs (2i, 2i+1); 1 half pairs (i, i + d/2)
+    int scaled;  // Llama-3 frequency-dependent scaling on/off
+};
+
+// Kernel kinds for the timing hooks.
+enum KernelKind { K_ROPE_APPEND = 0, K_DECODE_PARTIAL = 1, K_DECODE_COMBINE = 2, K_PREFILL = 3, K_KINDS = 4 };
+
+// Timing hooks (no-ops unless enabled through gqa_profile_enable).
+void prof_begin(int kind, hipStream_t st);
+void prof_end(int kind, hipStream_t st);
+
+// ---- rope_append ---------------------------------------------------------------
+hipError_t launch_rope_append(const uint16_t* q, uint16_t* q_rot, const uint16_t* k_new, const uint16_t* v_new,
+                              uint16_t* k_cache, uint16_t* v_cache, const int32_t* past_len, int max_past_len,
+                              int B, int n_q, int n_kv, int T, int d, int S, const RopeDev& rope, hipStream_t st);
+
+// ---- decode (split-K partials + combine) ----------------------------------------
+// Largest batch one decode launch handles; larger batches are processed in
+// slices of this many sequences.
+constexpr int DECODE_MAX_B = 2048;
+// Upper bound on the number of split-K workgroups (sizes the workspace).
+constexpr int DECODE_MAX_WG = 2048;
+
+struct DecodePlan {
+    int hgw;   // query heads per wave (1..4)
+    int nhg;   // head groups per workgroup (1, 2 or 4)
+    int gc;    // heads per segment = hgw * nhg
+    int nhc;   // segments per (sequence, KV head) = g / gc
+    int rg;    // row groups per workgroup = 4 / nhg
+    int rec;   // floats per partial record = d + 4
+    size_t slot_floats;  // rg * gc * rec
+};
+DecodePlan decode_plan(int n_q, int n_kv, int d);
+size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d);
+hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
+                         const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
+                         int n_kv, int d, int S, float scale, int wg_override, hipStream_t st);
+
+// ---- prefill -----------------------------------------------------------------------
+hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
+                          const int32_t* past_len, int max_past_len, uint16_t* out, int B, int n_q, int n_kv, int T,
+                          int d, int S, float scale, hipStream_t st);
+
+}  // namespace gqa

@@ -1,0 +1,299 @@
+// Chunked-prefill attention on gfx950 bf16 MFMA.
+//
+// What is computed ([ATL] "Llama 3 8B - KV cache", Transformer.forward excerpt
+// and its comment on the mask under a cache; [KV] "Llama 3.1 8B KV cache",
+// "The cache itself is concatenation"): new row t of sequence b sits at
+// position past_len[b] + t and attends to cache rows 0 .. past_len[b] + t of
+// KV head floor(h / g).  The score block is rectangular, T x (past_len + T).
+//
+// How: a workgroup (4 waves) owns 128 query rows of one (sequence, KV head):
+// up to 128/g positions times the g heads of the group, so every K/V tile it
+// stages serves all heads that share it.  Per 64-key tile:
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = the
+//                  wave's 32 query rows held in registers)
+//   online softmax per query row (each lane holds one query row per 16-row
+//                  block, so only two cross-lane steps are needed)
+//   O^T += V^T P^T (A = V^T from a transposed LDS copy of the V tile,
+//                  B = the softmax weights already in the right lanes, split
+//                  into a bf16 high part and a bf16 remainder so that the
+//                  weights enter the product with ~16 significant bits)
+// Tiles entirely above every row's causal bound are never loaded; tiles that
+// straddle a bound are masked element-wise.  The next tile's global loads are
+// in flight while the current tile is computed.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gqa {
+
+namespace {
+
+constexpr int KT = 64;        // keys per tile
+constexpr int NTHR = 256;     // 4 waves
+constexpr int ROWS = 128;     // query rows per workgroup (32 per wave)
+constexpr float LOG2E_P = 1.4426950408889634f;
+
+// K tile: [64 keys][D] bf16 in 16-byte pieces; piece c of key r sits at c ^ (r mod PPR)
+template <int PPR>
+__device__ __forceinline__ int kpos(int key, int c) {
+    return key * PPR + (c ^ (key & (PPR - 1)));
+}
+// V^T tile: [D dims][64 keys] bf16 in 8-byte units of 4 keys; unit u of dim row d sits at u ^ (d mod 16)
+__device__ __forceinline__ int vt_byte(int dim, int unit) { return dim * 128 + ((unit ^ (dim & 15)) << 3); }
+
+template <int D>
+__global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __restrict__ q_rot,
+                                                          const uint16_t* __restrict__ k_cache,
+                                                          const uint16_t* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ past_len, int pmax,
+                                                          uint16_t* __restrict__ out, int n_q, int n_kv, int T,
+                                                          int S, int hpw, int tq, int n_tq, float scale_log2) {
+    constexpr int PPR = D / 8;     // 16-byte pieces per key row
+    constexpr int KS = D / 32;     // MFMA k-steps over d
+    constexpr int DB = D / 16;     // 16-dim blocks of the output
+    constexpr int K_LOADS = KT * PPR / NTHR;        // 16-byte K loads per thread
+    constexpr int V_ITEMS = (KT / 2) * PPR / NTHR;  // (key pair, piece) items per thread
+    __shared__ uint4 s_k[KT * PPR];
+    __shared__ __align__(16) unsigned char s_vt[D * 128];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int g = n_q / n_kv;
+    const int tq_idx = n_tq - 1 - (int)(blockIdx.x % n_tq);  // longest rows first
+    const int hc = blockIdx.x / n_tq;
+    const int j = blockIdx.y, b = blockIdx.z;
+    int P = past_len[b];
+    if (P < 0 || P > pmax) return;  // caller error: nothing is written for this sequence
+    const int t0 = tq_idx * tq;
+
+    // ---- this lane's query row in each of its two 16-row blocks
+    int row_t[2], row_h[2];
+    bool row_ok[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int rho = wave * 32 + nb * 16 + l16;
+        const int hl = rho / tq, tl = rho % tq;
+        const int h = hc * hpw + hl;
+        row_ok[nb] = rho < hpw * tq && hl < hpw && h < g && t0 + tl < T;
+        row_h[nb] = j * g + (h < g ? h : g - 1);
+        row_t[nb] = row_ok[nb] ? t0 + tl : (t0 < T ? t0 : T - 1);
+    }
+    const int t_hi = (t0 + tq < T ? t0 + tq : T) - 1;
+    const int kv_end = P + t_hi + 1;            // keys visible to the last row of this workgroup
+    const int n_tiles = (kv_end + KT - 1) / KT;
+    const int first_masked_tile = (P + t0 + 1) / KT;  // tiles before this one are fully visible
+
+    // ---- Q^T operand: 8 dims of one query row per lane and k-step
+    bf16x8_t qop[2][KS];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const uint4* src = reinterpret_cast<const uint4*>(q_rot + ((size_t)row_h[nb] * T + row_t[nb]) * D +
+                                                         (size_t)b * n_q * T * D);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 x = src[4 * ks + lq];
+            qop[nb][ks] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+
+    const uint16_t* kbase = k_cache + (size_t)(b * n_kv + j) * S * D;
+    const uint16_t* vbase = v_cache + (size_t)(b * n_kv + j) * S * D;
+
+    uint4 kst[K_LOADS];
+    uint4 vst[V_ITEMS][2];
+    auto load = [&](int tile) {
+        const int key0 = tile * KT;
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) {
+            const int pi = tid + NTHR * i;
+            const int key = pi / PPR, c = pi % PPR;
+            kst[i] = key0 + key < kv_end ? *reinterpret_cast<const uint4*>(kbase + (size_t)(key0 + key) * D + 8 * c)
+                                         : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < V_ITEMS; ++i) {
+            const int it = tid + NTHR * i;
+            const int kp = it % (KT / 2), c = it / (KT / 2);
+            const int k0 = key0 + 2 * kp;
+            vst[i][0] = k0 < kv_end ? *reinterpret_cast<const uint4*>(vbase + (size_t)k0 * D + 8 * c)
+                                    : make_uint4(0, 0, 0, 0);
+            vst[i][1] = k0 + 1 < kv_end ? *reinterpret_cast<const uint4*>(vbase + (size_t)(k0 + 1) * D + 8 * c)
+                                        : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) {
+            const int pi = tid + NTHR * i;
+            s_k[kpos<PPR>(pi / PPR, pi % PPR)] = kst[i];
+        }
+#pragma unroll
+        for (int i = 0; i < V_ITEMS; ++i) {
+            const int it = tid + NTHR * i;
+            const int kp = it % (KT / 2), c = it / (KT / 2);
+            const uint32_t a[4] = {vst[i][0].x, vst[i][0].y, vst[i][0].z, vst[i][0].w};
+            const uint32_t bq[4] = {vst[i][1].x, vst[i][1].y, vst[i][1].z, vst[i][1].w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                // dims 8c+2x and 8c+2x+1, keys 2kp and 2kp+1
+                const uint32_t lo = (a[x] & 0xffffu) | (bq[x] << 16);
+                const uint32_t hi = (a[x] >> 16) | (bq[x] & 0xffff0000u);
+                const int d0 = 8 * c + 2 * x;
+                const int unit = kp >> 1, sub = (kp & 1) * 4;
+                *reinterpret_cast<uint32_t*>(s_vt + vt_byte(d0, unit) + sub) = lo;
+                *reinterpret_cast<uint32_t*>(s_vt + vt_byte(d0 + 1, unit) + sub) = hi;
+            }
+        }
+    };
+
+    f32x4_t oacc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    load(0);
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        __syncthreads();
+        store();
+        __syncthreads();
+        if (tile + 1 < n_tiles) load(tile + 1);
+
+        // ---- S^T = K Q^T for 64 keys x 32 query rows
+        f32x4_t sacc[4][2];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) sacc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s_k[kpos<PPR>(16 * mb + l16, 4 * ks + lq)]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    sacc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[nb][ks], sacc[mb][nb], 0, 0, 0);
+            }
+        }
+
+        // ---- scale, mask, online softmax per query row
+        const int key0 = tile * KT;
+        const bool masked_tile = tile >= first_masked_tile;
+        // [hi/lo][kb][nb][word]: the weights as PV B operands, split p = hi + lo with both parts
+        // in bf16 so the product with V keeps ~16 significant bits of p
+        uint32_t pk[2][2][2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int lim = P + row_t[nb];  // last visible key of this row
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float s = sacc[mb][nb][i] * scale_log2;
+                    if (masked_tile && key0 + 16 * mb + 4 * lq + i > lim) s = -INFINITY;
+                    sacc[mb][nb][i] = s;
+                    mx = fmaxf(mx, s);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m_run[nb], mx);  // finite: key 0 is visible to every row
+            const float alpha = fast_exp2(m_run[nb] - mn);
+            m_run[nb] = mn;
+            float ps = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(sacc[mb][nb][i] - mn);
+                    ps += p[i];
+                }
+                uint32_t hb[4], lb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    hb[i] = f32_to_bf16_rne(p[i]);
+                    lb[i] = f32_to_bf16_rne(p[i] - __uint_as_float(hb[i] << 16));
+                }
+                pk[0][mb >> 1][nb][(mb & 1) * 2 + 0] = hb[0] | (hb[1] << 16);
+                pk[0][mb >> 1][nb][(mb & 1) * 2 + 1] = hb[2] | (hb[3] << 16);
+                pk[1][mb >> 1][nb][(mb & 1) * 2 + 0] = lb[0] | (lb[1] << 16);
+                pk[1][mb >> 1][nb][(mb & 1) * 2 + 1] = lb[2] | (lb[3] << 16);
+            }
+            l_run[nb] = l_run[nb] * alpha + ps;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db][nb] *= alpha;
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            bf16x8_t bop[2][2];
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    bop[hl][nb] = __builtin_bit_cast(
+                        bf16x8_t, make_uint4(pk[hl][kb][nb][0], pk[hl][kb][nb][1], pk[hl][kb][nb][2], pk[hl][kb][nb][3]));
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int dim = 16 * db + l16;
+                const uint2 u0 = *reinterpret_cast<const uint2*>(s_vt + vt_byte(dim, 8 * kb + lq));
+                const uint2 u1 = *reinterpret_cast<const uint2*>(s_vt + vt_byte(dim, 8 * kb + 4 + lq));
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[0][nb], oacc[db][nb], 0, 0, 0);
+                    oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[1][nb], oacc[db][nb], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- normalise and store: lane holds dims 16db + 4*lq + 0..3 of its row
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        float l = l_run[nb];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (!row_ok[nb]) continue;
+        const float inv = 1.f / l;
+        uint16_t* dst = out + ((size_t)b * n_q * T + (size_t)row_h[nb] * T + row_t[nb]) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const f32x4_t o = oacc[db][nb];
+            *reinterpret_cast<uint2*>(dst + 16 * db + 4 * lq) =
+                make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
+                          const int32_t* past_len, int max_past_len, uint16_t* out, int B, int n_q, int n_kv, int T,
+                          int d, int S, float scale, hipStream_t st) {
+    const int g = n_q / n_kv;
+    const int hpw = g < ROWS ? g : ROWS;  // heads per workgroup
+    const int tq = ROWS / hpw;            // positions per workgroup
+    const int n_tq = (T + tq - 1) / tq;
+    const int n_hc = (g + hpw - 1) / hpw;
+    const float scale_log2 = scale * LOG2E_P;
+    for (int b0 = 0; b0 < B; b0 += 65535) {
+        const int nb = (B - b0) < 65535 ? (B - b0) : 65535;
+        dim3 grid((unsigned)(n_tq * n_hc), n_kv, nb);
+        const size_t qo = (size_t)b0 * n_q * T * d, co = (size_t)b0 * n_kv * S * d;
+        prof_begin(K_PREFILL, st);
+        if (d == 128)
+            hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(NTHR), 0, st, q_rot + qo, k_cache + co,
+                               v_cache + co, past_len + b0, max_past_len, out + qo, n_q, n_kv, T, S, hpw, tq, n_tq,
+                               scale_log2);
+        else
+            hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(NTHR), 0, st, q_rot + qo, k_cache + co, v_cache + co,
+                               past_len + b0, max_past_len, out + qo, n_q, n_kv, T, S, hpw, tq, n_tq, scale_log2);
+        prof_end(K_PREFILL, st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace gqa

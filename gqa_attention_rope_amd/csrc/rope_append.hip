@@ -1,0 +1,164 @@
+// Fused RoPE of q and the new k at offset past_len, plus the cache append of
+// the rotated k rows and the v rows.
+//
+// [KV] "Llama 3.1 8B KV cache", section "RoPE has to know where it is": the
+// rotary angle of a new token is its absolute position past_len + t times the
+// pair frequency theta^(-2i/d).  [ATL] "Llama 3 8B - KV cache", cache formula:
+// the rotated keys and the values are written at rows past_len .. past_len+T-1
+// and nothing else in the cache changes.
+//
+// One workgroup handles one token (t, b): it computes the d/2 angles of its
+// position once, in fp64, keeps cos/sin in LDS, and then every thread turns
+// 8 pairs at a time (two 16-byte loads, two 16-byte stores) over all n_q query
+// heads and n_kv key heads, and copies the value rows.  All global accesses
+// are 16-byte and contiguous along d.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gqa {
+
+namespace {
+
+// Pair frequency, optionally with Llama-3 scaling ([KV] "Training details that
+// matter" names the factor and the two cutoffs; the reading of the rule: short
+// wavelengths keep their frequency, long ones are divided by the factor, and
+// the band between blends the two linearly in original_max_pos / wavelength).
+__device__ double pair_frequency(int i, int d, const RopeDev& rp) {
+    double f = pow(rp.theta, -(2.0 * (double)i) / (double)d);
+    if (rp.scaled) {
+        const double two_pi = 6.283185307179586476925286766559;
+        double wavelength = two_pi / f;
+        double long_cut = rp.original_max_pos / rp.low_freq_factor;
+        double short_cut = rp.original_max_pos / rp.high_freq_factor;
+        if (wavelength < short_cut) {
+            // unchanged
+        } else if (wavelength > long_cut) {
+            f = f / rp.factor;
+        } else {
+            double s = (rp.original_max_pos / wavelength - rp.low_freq_factor) /
+                       (rp.high_freq_factor - rp.low_freq_factor);
+            f = (1.0 - s) * f / rp.factor + s * f;
+        }
+    }
+    return f;
+}
+
+// (a, b) -> (a cos - b sin, a sin + b cos), fp64, each output rounded once to bf16.
+__device__ __forceinline__ void turn(float a, float b, double c, double s, uint32_t& ra, uint32_t& rb) {
+    double da = (double)a, db = (double)b;
+    ra = f64_to_bf16_rne(da * c - db * s);
+    rb = f64_to_bf16_rne(da * s + db * c);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uint16_t* q_rot,
+                                                          const uint16_t* __restrict__ k_new,
+                                                          const uint16_t* __restrict__ v_new,
+                                                          uint16_t* __restrict__ k_cache,
+                                                          uint16_t* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ past_len, int max_past_len,
+                                                          int n_q, int n_kv, int T, int S, RopeDev rp) {
+    constexpr int HALF = D / 2;
+    constexpr int ITEMS_PER_HEAD = D / 16;  // 8 pairs (16 values) per item
+    __shared__ double s_cos[HALF];
+    __shared__ double s_sin[HALF];
+
+    const int t = blockIdx.x;
+    const int b = blockIdx.y;
+    const int P = past_len[b];
+    if (P < 0 || P > max_past_len) return;  // caller error: write nothing for this sequence
+    const int pos = P + t;                  // < max_past_len + T <= S (checked on the host)
+
+    for (int i = threadIdx.x; i < HALF; i += blockDim.x) {
+        double ang = (double)pos * pair_frequency(i, D, rp);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        s_cos[i] = cs;
+        s_sin[i] = sn;
+    }
+    __syncthreads();
+
+    const int heads = n_q + 2 * n_kv;
+    const int items = heads * ITEMS_PER_HEAD;
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+        const int head = it / ITEMS_PER_HEAD;
+        const int c = it % ITEMS_PER_HEAD;
+        if (head >= n_q + n_kv) {  // value row: bit copy of 16 values
+            const int j = head - n_q - n_kv;
+            const uint4* src = reinterpret_cast<const uint4*>(v_new + ((size_t)(b * n_kv + j) * T + t) * D) + 2 * c;
+            uint4* dst = reinterpret_cast<uint4*>(v_cache + ((size_t)(b * n_kv + j) * S + pos) * D) + 2 * c;
+            uint4 x0 = src[0], x1 = src[1];
+            dst[0] = x0;
+            dst[1] = x1;
+            continue;
+        }
+        const uint16_t* src;
+        uint16_t* dst;
+        if (head < n_q) {
+            src = q + ((size_t)(b * n_q + head) * T + t) * D;
+            dst = q_rot + ((size_t)(b * n_q + head) * T + t) * D;
+        } else {
+            const int j = head - n_q;
+            src = k_new + ((size_t)(b * n_kv + j) * T + t) * D;
+            dst = k_cache + ((size_t)(b * n_kv + j) * S + pos) * D;
+        }
+        // two 16-byte pieces holding 8 (a, b) pairs
+        const int off0 = rp.layout == 0 ? 16 * c : 8 * c;
+        const int off1 = rp.layout == 0 ? 16 * c + 8 : HALF + 8 * c;
+        uint4 x0 = *reinterpret_cast<const uint4*>(src + off0);
+        uint4 x1 = *reinterpret_cast<const uint4*>(src + off1);
+        uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t o[8];
+        if (rp.layout == 0) {
+            // interleaved: word m holds pair 8c + m as (lo, hi) = (a, b)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int i = 8 * c + m;
+                uint32_t ra, rb;
+                turn(bf_lo(w[m]), bf_hi(w[m]), s_cos[i], s_sin[i], ra, rb);
+                o[m] = ra | (rb << 16);
+            }
+        } else {
+            // half: value m of piece 0 pairs with value m of piece 1 (pair 8c + m)
+#pragma unroll
+            for (int m = 0; m < 8; m += 2) {
+                const int i = 8 * c + m;
+                uint32_t ra0, rb0, ra1, rb1;
+                turn(bf_lo(w[m / 2]), bf_lo(w[4 + m / 2]), s_cos[i], s_sin[i], ra0, rb0);
+                turn(bf_hi(w[m / 2]), bf_hi(w[4 + m / 2]), s_cos[i + 1], s_sin[i + 1], ra1, rb1);
+                o[m / 2] = ra0 | (ra1 << 16);
+                o[4 + m / 2] = rb0 | (rb1 << 16);
+            }
+        }
+        *reinterpret_cast<uint4*>(dst + off0) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(dst + off1) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rope_append(const uint16_t* q, uint16_t* q_rot, const uint16_t* k_new, const uint16_t* v_new,
+                              uint16_t* k_cache, uint16_t* v_cache, const int32_t* past_len, int max_past_len,
+                              int B, int n_q, int n_kv, int T, int d, int S, const RopeDev& rope, hipStream_t st) {
+    // grid.y is limited to 65535 sequences per launch: slice larger batches
+    for (int b0 = 0; b0 < B; b0 += 65535) {
+        const int nb = (B - b0) < 65535 ? (B - b0) : 65535;
+        dim3 grid(T, nb);
+        const size_t qo = (size_t)b0 * n_q * T * d, ko = (size_t)b0 * n_kv * T * d, co = (size_t)b0 * n_kv * S * d;
+        prof_begin(K_ROPE_APPEND, st);
+        if (d == 128)
+            hipLaunchKernelGGL(rope_append_kernel<128>, grid, dim3(256), 0, st, q + qo, q_rot + qo, k_new + ko,
+                               v_new + ko, k_cache + co, v_cache + co, past_len + b0, max_past_len, n_q, n_kv, T, S,
+                               rope);
+        else
+            hipLaunchKernelGGL(rope_append_kernel<64>, grid, dim3(256), 0, st, q + qo, q_rot + qo, k_new + ko,
+                               v_new + ko, k_cache + co, v_cache + co, past_len + b0, max_past_len, n_q, n_kv, T, S,
+                               rope);
+        prof_end(K_ROPE_APPEND, st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace gqa

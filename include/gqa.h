@@ -1,0 +1,183 @@
+/*
+ * gqa.h -- C ABI of libgqa: one grouped-query attention step with RoPE over a
+ * preallocated bf16 KV cache, on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows (title, then section / formula / excerpt):
+ *   [KV]   "Llama 3.1 8B KV cache" (alijanati.com)
+ *   [ATL]  "Llama 3 8B - KV cache" (OpenModelAtlas, decode at position 1000)
+ *   [REP]  "Llama 3.1 8B - Repeat heads" (OpenModelAtlas)
+ *   [EP18] "Grouped-query attention: a smaller KV cache" (mvgpt, episode 18)
+ *   [P7]   "Part 7: The Modern Decoder Block" (openlearn)
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as device pointers to 16-bit patterns (no C bf16
+ *     type is needed); int32 tensors as device pointers to int32_t.
+ *   - Every tensor is dense, row-major, and its device pointer is 16-byte
+ *     aligned.  Shapes:
+ *        q, q_rot, out  [B, n_q,  T, d]
+ *        k_new, v_new   [B, n_kv, T, d]
+ *        k_cache,v_cache[B, n_kv, S, d]   (keys are stored already rotated)
+ *        past_len       [B]  int32, rows already cached for each sequence
+ *   - n_q = g * n_kv; query head h reads KV head floor(h / g) ([REP] formula;
+ *     [EP18] "Our six heads, three ways").  No copy of a KV head is made.
+ *   - d is 64 or 128 (the kernels are built for these two head sizes).
+ *   - past_len lives in device memory so that calls can be captured and
+ *     replayed; max_past_len is the host-side upper bound the caller vouches
+ *     for (past_len[b] <= max_past_len for every b).  Every launch is sized
+ *     from it, and kernels never touch a cache row >= S.  A past_len[b] outside
+ *     [0, max_past_len] is a caller error: rows it would address are skipped
+ *     rather than written out of bounds, and the outputs of that sequence are
+ *     unspecified.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued on it; no call synchronises, allocates or frees
+ *     memory.  The caller owns every buffer, including workspaces.
+ *   - Calls on one stream are ordered: gqa_rope_append must be enqueued before
+ *     the attention call that reads the rows it writes.
+ *   - Return value: GQA_OK or a negative status (below).  All argument checks
+ *     run on the host before any HIP call; a failed check launches nothing.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define GQA_OK 0
+#define GQA_ERR_INVALID_ARG (-1) /* null/misaligned pointer, size <= 0, odd d, bad RoPE params */
+#define GQA_ERR_GROUP (-2)       /* n_q is not a multiple of n_kv ([EP18] "Grouped-query attention in code") */
+#define GQA_ERR_HEAD_DIM (-3)    /* d is not 64 or 128 */
+#define GQA_ERR_RANGE (-4)       /* max_past_len < 0, or max_past_len + T > S */
+#define GQA_ERR_WORKSPACE (-5)   /* workspace smaller than gqa_decode_workspace_bytes() */
+#define GQA_ERR_HIP (-6)         /* no device, launch or runtime failure; see gqa_status_string */
+
+/* ---- RoPE parameters ------------------------------------------------- */
+#define GQA_ROPE_INTERLEAVED 0 /* pair i is dims (2i, 2i+1) */
+#define GQA_ROPE_HALF 1        /* pair i is dims (i, i + d/2) */
+
+typedef struct gqa_rope_params {
+    double theta;            /* base: freq_i = theta^(-2i/d)  ([KV] "RoPE has to know where it is") */
+    int layout;              /* GQA_ROPE_INTERLEAVED or GQA_ROPE_HALF ([P7] module L7.3) */
+    int scaled;              /* 0: plain RoPE; 1: Llama-3 frequency-dependent scaling below */
+    double factor;           /* Llama-3 scaling: long wavelengths are divided by this (> 0) */
+    double low_freq_factor;  /* wavelengths above original_max_pos / low_freq_factor: fully scaled */
+    double high_freq_factor; /* wavelengths below original_max_pos / high_freq_factor: unchanged */
+    double original_max_pos; /* context length the base model was trained on (> 0) */
+} gqa_rope_params;
+
+/*
+ * gqa_rope_append -- rotate q and the new k at their positions and write the
+ * rotated k and the v rows into the cache.
+ *
+ * [KV] "RoPE has to know where it is": new token t of sequence b sits at
+ * position p = past_len[b] + t.  Pair i of every head of q and k_new is turned
+ * by the angle p * freq_i: (a, b) -> (a cos - b sin, a sin + b cos).
+ * [ATL] cache formula: cache rows p = past_len[b] .. past_len[b]+T-1 receive
+ * the rotated keys and the values; no other cache row is touched.
+ *
+ * Precision: frequencies, angles, sin/cos and the rotation are computed in
+ * fp64 on the device and each result is rounded once to bf16 (nearest, ties
+ * to even).  v rows are copied bit for bit.
+ *
+ *   q        in   [B, n_q, T, d] bf16
+ *   q_rot    out  [B, n_q, T, d] bf16, may equal q (rotated in place)
+ *   k_new    in   [B, n_kv, T, d] bf16 (unrotated)
+ *   v_new    in   [B, n_kv, T, d] bf16
+ *   k_cache  in/out [B, n_kv, S, d] bf16
+ *   v_cache  in/out [B, n_kv, S, d] bf16
+ *   past_len in   [B] int32 (device)
+ *   rope     in   host pointer; theta > 0, layout valid; when scaled:
+ *                 factor > 0, 0 < low_freq_factor < high_freq_factor,
+ *                 original_max_pos > 0
+ * Errors: INVALID_ARG, GROUP, HEAD_DIM, RANGE (max_past_len + T > S), HIP.
+ */
+int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, const int32_t* past_len, int max_past_len, int B, int n_q, int n_kv, int T,
+                    int d, int S, const gqa_rope_params* rope, void* stream);
+
+/*
+ * gqa_decode_workspace_bytes -- bytes of device workspace gqa_decode_attn
+ * needs for this shape (0 when the shape is invalid).  The size depends only
+ * on the arguments and on library constants, not on past_len.
+ */
+size_t gqa_decode_workspace_bytes(int B, int n_q, int n_kv, int d, int S);
+
+/*
+ * gqa_decode_attn -- one new query token per sequence attends to cache rows
+ * 0 .. past_len[b] (the row written by the matching gqa_rope_append included).
+ *
+ * [ATL] prose: the decode call at position p reads rows 0..p; with one new
+ * token there is nothing to mask inside that range ([ATL] Transformer.forward
+ * excerpt builds no mask when seqlen is 1).  Scores are q.k * scale, softmax
+ * over the rows, then the weighted sum of the value rows ([KV] "The cache
+ * itself is concatenation").  Each KV head's rows are read from memory once
+ * for all g query heads of its group.
+ *
+ * The work is split over the rows ("split-K"); each split writes
+ * (max, sum, partial output) records into the workspace, and a second kernel
+ * merges them in a fixed order, so results are bitwise reproducible.
+ *
+ *   q_rot     in  [B, n_q, 1, d] bf16 (already rotated)
+ *   k_cache   in  [B, n_kv, S, d] bf16;  v_cache likewise
+ *   past_len  in  [B] int32 (device); rows 0..past_len[b] are attended
+ *   out       out [B, n_q, 1, d] bf16
+ *   workspace device scratch of at least gqa_decode_workspace_bytes(...)
+ *   scale     score scale; <= 0 selects 1/sqrt(d)
+ * Errors: INVALID_ARG, GROUP, HEAD_DIM, RANGE (max_past_len + 1 > S),
+ *         WORKSPACE, HIP.
+ */
+int gqa_decode_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                    int max_past_len, void* out, void* workspace, size_t workspace_bytes, int B, int n_q, int n_kv,
+                    int d, int S, float scale, void* stream);
+
+/*
+ * gqa_prefill_attn -- T new query tokens per sequence attend to the cache
+ * under the rectangular causal mask: row t (position past_len[b] + t) sees
+ * cache rows 0 .. past_len[b] + t ([ATL] Transformer.forward excerpt and its
+ * comment on the mask with a cache).  QK^T and PV run on bf16 MFMA with fp32
+ * accumulation; the softmax weights enter the PV product as a bf16 high part
+ * plus a bf16 remainder (about 16 significant bits).
+ *
+ *   q_rot   in  [B, n_q, T, d] bf16 (already rotated)
+ *   k_cache in  [B, n_kv, S, d] bf16 (rows up to past_len[b]+T-1 written)
+ *   out     out [B, n_q, T, d] bf16
+ *   scale   <= 0 selects 1/sqrt(d)
+ * Errors: INVALID_ARG, GROUP, HEAD_DIM, RANGE (max_past_len + T > S), HIP.
+ */
+int gqa_prefill_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                     int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
+                     void* stream);
+
+/* Human-readable text for a status code; for GQA_ERR_HIP it includes the
+ * last HIP error message recorded by this thread.  Never NULL. */
+const char* gqa_status_string(int status);
+
+/*
+ * Kernel timing -- measurement support for benchmarks.  While enabled, every
+ * kernel launch of this library is bracketed by two HIP events recorded on
+ * the launch stream; gqa_profile_read synchronises those events and returns
+ * the summed device time and launch count of one kernel kind.
+ *   kind: 0 rope_append, 1 decode split-K partials, 2 decode combine,
+ *         3 prefill.
+ * Not thread-safe; for single-threaded benchmark drivers.
+ */
+int gqa_profile_enable(int on);
+int gqa_profile_read(int kind, double* total_ms, long long* launches);
+int gqa_profile_reset(void);
+
+/*
+ * Launch-shape override for tests and tuning: the number of workgroups the
+ * decode split-K kernel uses (0 = the occupancy-derived default).  Values
+ * above the library maximum are clamped.  Results do not depend on it beyond
+ * floating-point rounding.  Returns the value in effect.
+ */
+int gqa_set_decode_workgroups(int n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQA_H */

@@ -1,0 +1,141 @@
+"""The C ABI library loads, exports what include/gqa.h declares, and rejects bad
+arguments on the host before any HIP call (CPU only, no device needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_attention_rope_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gq.LIB_PATH), reason="libgqa.so not built")
+
+FAKE = 0x10000  # aligned, never dereferenced on the host
+P = ctypes.c_void_p
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gqa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = gq.lib()
+    names = header_functions()
+    assert set(names) == set(gq.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def rope(theta=5.0e5, layout=0, scaled=0, factor=8.0, low=1.0, high=4.0, orig=8192.0):
+    p = gq.GqaRopeParams()
+    p.theta, p.layout, p.scaled = theta, layout, scaled
+    p.factor, p.low_freq_factor, p.high_freq_factor, p.original_max_pos = factor, low, high, orig
+    return p
+
+
+def append(**kw):
+    a = dict(q=FAKE, q_rot=FAKE, k_new=FAKE, v_new=FAKE, kc=FAKE, vc=FAKE, pl=FAKE, maxp=10, B=2, n_q=8, n_kv=2,
+             T=1, d=128, S=64, rope=rope())
+    a.update(kw)
+    r = a["rope"]
+    return gq.lib().gqa_rope_append(P(a["q"]), P(a["q_rot"]), P(a["k_new"]), P(a["v_new"]), P(a["kc"]), P(a["vc"]),
+                                    P(a["pl"]), a["maxp"], a["B"], a["n_q"], a["n_kv"], a["T"], a["d"], a["S"],
+                                    None if r is None else ctypes.byref(r), None)
+
+
+def decode(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, pl=FAKE, maxp=10, out=FAKE, ws=FAKE, wsb=1 << 40, B=2, n_q=8, n_kv=2, d=128,
+             S=64, scale=0.0)
+    a.update(kw)
+    return gq.lib().gqa_decode_attn(P(a["q"]), P(a["kc"]), P(a["vc"]), P(a["pl"]), a["maxp"], P(a["out"]),
+                                    P(a["ws"]), a["wsb"], a["B"], a["n_q"], a["n_kv"], a["d"], a["S"], a["scale"],
+                                    None)
+
+
+def prefill(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, pl=FAKE, maxp=10, out=FAKE, B=2, n_q=8, n_kv=2, T=4, d=128, S=64, scale=0.0)
+    a.update(kw)
+    return gq.lib().gqa_prefill_attn(P(a["q"]), P(a["kc"]), P(a["vc"]), P(a["pl"]), a["maxp"], P(a["out"]), a["B"],
+                                     a["n_q"], a["n_kv"], a["T"], a["d"], a["S"], a["scale"], None)
+
+
+INV, GRP, HD, RNG, WS, HIP = (gq.GQA_ERR_INVALID_ARG, gq.GQA_ERR_GROUP, gq.GQA_ERR_HEAD_DIM, gq.GQA_ERR_RANGE,
+                              gq.GQA_ERR_WORKSPACE, gq.GQA_ERR_HIP)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INV), (dict(kc=0), INV), (dict(pl=0), INV), (dict(rope=None), INV), (dict(q_rot=FAKE + 8), INV),
+    (dict(B=0), INV), (dict(n_q=-1), INV), (dict(T=0), INV), (dict(S=0), INV), (dict(d=127), INV),
+    (dict(n_q=6, n_kv=4), GRP), (dict(d=96), HD), (dict(d=256), HD),
+    (dict(maxp=-1), RNG), (dict(maxp=64, T=1, S=64), RNG), (dict(maxp=60, T=5, S=64), RNG),
+    (dict(rope=rope(theta=0.0)), INV), (dict(rope=rope(theta=float("nan"))), INV), (dict(rope=rope(layout=2)), INV),
+    (dict(rope=rope(scaled=1, factor=0.0)), INV), (dict(rope=rope(scaled=1, low=4.0, high=1.0)), INV),
+    (dict(rope=rope(scaled=1, orig=0.0)), INV),
+])
+def test_rope_append_validation(kw, code):
+    assert append(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INV), (dict(out=0), INV), (dict(ws=0), INV), (dict(out=FAKE + 4), INV), (dict(pl=FAKE + 2), INV),
+    (dict(B=0), INV), (dict(d=63), INV), (dict(n_q=8, n_kv=3), GRP), (dict(d=32), HD),
+    (dict(maxp=64, S=64), RNG), (dict(maxp=-5), RNG), (dict(wsb=0), WS), (dict(scale=float("inf")), INV),
+])
+def test_decode_validation(kw, code):
+    assert decode(**kw) == code
+
+
+def test_decode_workspace_query():
+    L = gq.lib()
+    n = L.gqa_decode_workspace_bytes(32, 32, 8, 128, 8192)
+    assert n > 0 and n % 16 == 0
+    assert decode(wsb=L.gqa_decode_workspace_bytes(2, 8, 2, 128, 64) - 1) == WS
+    assert L.gqa_decode_workspace_bytes(2, 8, 3, 128, 64) == 0
+    assert L.gqa_decode_workspace_bytes(2, 8, 2, 96, 64) == 0
+    # batches beyond one launch's slice reuse the workspace: size stops growing
+    assert L.gqa_decode_workspace_bytes(4096, 32, 8, 128, 64) == L.gqa_decode_workspace_bytes(2048, 32, 8, 128, 64)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INV), (dict(vc=FAKE + 1), INV), (dict(T=0), INV), (dict(n_q=8, n_kv=16), GRP), (dict(d=80), HD),
+    (dict(maxp=61, T=4, S=64), RNG), (dict(scale=float("nan")), INV),
+])
+def test_prefill_validation(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(gq.gqa_status_string(s), str) and gq.gqa_status_string(s)
+    assert "multiple" in gq.gqa_status_string(gq.GQA_ERR_GROUP)
+
+
+def test_valid_call_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert append() == HIP
+    assert decode() == HIP
+    assert prefill() == HIP
+    assert gq.gqa_status_string(HIP)
+
+
+def test_python_binding_validates_before_calling():
+    import torch
+    with pytest.raises(ValueError):
+        gq.gqa_decode_attn(torch.zeros(1, 2, 2, 64, dtype=torch.bfloat16), torch.zeros(1, 1, 8, 64),
+                           torch.zeros(1, 1, 8, 64), torch.zeros(1, dtype=torch.int32), 3)
+    with pytest.raises(ValueError):
+        gq.gqa_prefill_attn(torch.zeros(1, 2, 2, 64, dtype=torch.float32), torch.zeros(1, 1, 8, 64),
+                            torch.zeros(1, 1, 8, 64), torch.zeros(1, dtype=torch.int32), 3)
+
+
+def test_decode_workgroup_override_clamps():
+    assert gq.gqa_set_decode_workgroups(-3) == 0
+    assert gq.gqa_set_decode_workgroups(10 ** 6) > 0
+    assert gq.gqa_set_decode_workgroups(0) == 0

@@ -1,0 +1,314 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Bars: cache rows bit-exact for v and within 1 bf16 ulp for the rotated k (and
+for q_rot); attention outputs within max-abs 1e-2 AND max-rel 1e-2, where the
+relative error of an element is |e| / max(|ref|, 1e-2).  Every cache row the
+call must not read is filled with bf16 NaN first, so a stray read shows up
+as a non-finite output.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_rope_amd as gq
+from gqa_attention_rope_amd import synth
+from oracle import attend, bf16_to_f64, rope_append
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SCALED = synth.LLAMA3_SCALING
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def ulp_key(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    return np.where(b & 0x8000, 0x8000 - b, b)
+
+
+def max_ulp(a, b):
+    return int(np.max(np.abs(ulp_key(a) - ulp_key(b)))) if np.size(a) else 0
+
+
+def check_out(gpu_bits, ref, name):
+    g = bf16_to_f64(gpu_bits)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite outputs"
+    err = np.abs(g - ref)
+    rel = err / np.maximum(np.abs(ref), 1e-2)
+    bad = (err > 1e-2) | (rel > 1e-2)
+    say(f"  {name}: max abs {err.max():.3e}  max rel {rel.max():.3e}  n={err.size}")
+    assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} outside (abs {err.max():.3e}, rel {rel.max():.3e})"
+
+
+def dev(bits):
+    return synth.from_bits(bits, DEV)
+
+
+def past_dev(p):
+    return torch.as_tensor(np.asarray(p, dtype=np.int32), device=DEV)
+
+
+def make_inputs(B, n_q, n_kv, T, d, S, past, seed):
+    q = synth.bits(synth.normal_bf16((B, n_q, T, d), seed))
+    kn = synth.bits(synth.normal_bf16((B, n_kv, T, d), seed + 1))
+    vn = synth.bits(synth.normal_bf16((B, n_kv, T, d), seed + 2))
+    kc = synth.bits(synth.normal_bf16((B, n_kv, S, d), seed + 3))
+    vc = synth.bits(synth.normal_bf16((B, n_kv, S, d), seed + 4))
+    for b in range(B):  # rows the step must neither read nor write
+        kc[b, :, past[b] + T:] = synth.NAN_BF16
+        vc[b, :, past[b] + T:] = synth.NAN_BF16
+    return q, kn, vn, kc, vc
+
+
+# ---------------------------------------------------------------- rope_append
+
+APPEND_CASES = [
+    # B, n_q, n_kv, T, d, S, past, theta, layout, scaling
+    (1, 6, 2, 1, 64, 256, [255], 1.0e4, "interleaved", None),
+    (1, 32, 8, 1, 128, 8192, [1000], 5.0e5, "interleaved", None),
+    (3, 8, 2, 5, 128, 300, [0, 17, 290], 5.0e5, "interleaved", None),
+    (2, 8, 2, 3, 128, 8192, [8000, 4096], 5.0e5, "half", None),
+    (2, 16, 2, 1, 128, 8192, [8190, 5000], 5.0e5, "interleaved", SCALED),
+    (2, 6, 3, 4, 64, 100, [10, 96], 1.0e4, "half", SCALED),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}T{c[3]}d{c[4]}{c[8]}{'S' if c[9] else ''}")
+def test_rope_append_parity(case):
+    B, n_q, n_kv, T, d, S, past, theta, layout, scaling = case
+    say(f"rope_append {case[:8]} {layout} scaled={bool(scaling)}")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=11 + B + d)
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
+    kc_d, vc_d = dev(kc), dev(vc)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, past_dev(past), max(past), theta, layout, scaling)
+    torch.cuda.synchronize()
+    q_g, kc_g, vc_g = synth.bits(q_rot), synth.bits(kc_d), synth.bits(vc_d)
+    assert np.array_equal(vc_g, vc_ref), "value rows must be copied bit for bit and no other row touched"
+    rows = np.zeros(S, dtype=bool)
+    for b in range(B):
+        other = np.ones(S, dtype=bool)
+        other[past[b]:past[b] + T] = False
+        assert np.array_equal(kc_g[b][:, other], kc[b][:, other]), "rows outside the append must not change"
+        assert max_ulp(kc_g[b][:, ~other], kc_ref[b][:, ~other]) <= 1
+    assert max_ulp(q_g, q_ref) <= 1
+    say(f"  q_rot bit-exact {np.mean(q_g == q_ref):.6f}, k rows bit-exact "
+        f"{np.mean(kc_g == kc_ref):.6f}")
+
+
+def test_rope_append_in_place_q():
+    B, n_q, n_kv, T, d, S, past = 2, 8, 2, 3, 128, 64, [7, 40]
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=5)
+    q_ref, _, _ = rope_append(q, kn, vn, kc, vc, past, 5.0e5)
+    qd = dev(q)
+    out = gq.gqa_rope_append(qd, dev(kn), dev(vn), dev(kc), dev(vc), past_dev(past), max(past), 5.0e5, q_rot=qd)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == qd.data_ptr()
+    assert max_ulp(synth.bits(qd), q_ref) <= 1
+
+
+# ---------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    # B, n_q, n_kv, d, S, past, theta, layout, scaling
+    (1, 6, 2, 64, 256, [255], 1.0e4, "interleaved", None),            # tiny 6/2-head window
+    (1, 32, 8, 128, 8192, [1000], 5.0e5, "interleaved", None),        # one Llama-3.1-8B layer
+    (5, 32, 8, 128, 1100, [0, 63, 64, 65, 1098], 5.0e5, "interleaved", None),  # tile edges, L = 1
+    (3, 64, 8, 128, 600, [511, 300, 599], 5.0e5, "interleaved", SCALED),       # g = 8, scaled RoPE
+    (2, 8, 8, 128, 200, [150, 9], 5.0e5, "half", None),               # g = 1 (MHA)
+    (2, 6, 1, 64, 300, [299, 77], 1.0e4, "interleaved", None),        # g = 6 (MQA)
+    (2, 16, 1, 128, 300, [200, 1], 5.0e5, "interleaved", None),       # g = 16
+    (2, 10, 2, 128, 300, [100, 257], 5.0e5, "interleaved", None),     # g = 5: one head per segment
+    (2, 24, 2, 64, 200, [130, 66], 1.0e4, "half", None),              # g = 12
+]
+
+
+def run_decode_e2e(case, seed, wg=0):
+    B, n_q, n_kv, d, S, past, theta, layout, scaling = case
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed)
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
+    ref = attend(q_ref, kc_ref, vc_ref, past, n_kv)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    gq.gqa_set_decode_workgroups(wg)
+    try:
+        q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling)
+        out = gq.gqa_decode_attn(q_rot, kc_d, vc_d, pl, max(past))
+        torch.cuda.synchronize()
+    finally:
+        gq.gqa_set_decode_workgroups(0)
+    return synth.bits(out), ref, (q_rot, kc_d, vc_d, pl)
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}d{c[3]}P{max(c[5])}")
+def test_decode_end_to_end(case):
+    say(f"decode e2e {case[:6]}")
+    got, ref, _ = run_decode_e2e(case, seed=100 + case[1])
+    check_out(got, ref, "decode")
+
+
+@pytest.mark.parametrize("case", DECODE_CASES[:4], ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}P{max(c[5])}")
+def test_decode_kernel_isolated(case):
+    """Attention alone on synthetic already-rotated q and cache rows."""
+    B, n_q, n_kv, d, S, past = case[:6]
+    say(f"decode isolated {case[:6]}")
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=300 + n_q)
+    # the new row past_len is part of the attended range here: make it finite
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in range(B):
+        kc2[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 900 + b))
+        vc2[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 950 + b))
+    ref = attend(q, kc2, vc2, past, n_kv)
+    out = gq.gqa_decode_attn(dev(q), dev(kc2), dev(vc2), past_dev(past), max(past))
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, "decode isolated")
+
+
+def test_decode_workgroup_count_invariance_and_determinism():
+    case = (4, 32, 8, 128, 2000, [1999, 3, 700, 1500], 5.0e5, "interleaved", None)
+    say("decode workgroup sweep")
+    outs = []
+    for wg in (1, 3, 37, 256, 0):
+        got, ref, _ = run_decode_e2e(case, seed=77, wg=wg)
+        check_out(got, ref, f"decode wg={wg}")
+        outs.append(got)
+    again, _, _ = run_decode_e2e(case, seed=77, wg=0)
+    assert np.array_equal(again, outs[-1]), "same launch shape must give bitwise identical results"
+
+
+def test_decode_scale_argument():
+    B, n_q, n_kv, d, S, past = 2, 8, 2, 128, 128, [100, 20]
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=8)
+    for b in range(B):
+        kc[b, :, past[b]] = 0
+        vc[b, :, past[b]] = 0
+    ref = attend(q, kc, vc, past, n_kv, scale=0.3)
+    out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), scale=0.3)
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, "decode scale=0.3")
+
+
+# ---------------------------------------------------------------- prefill
+
+PREFILL_CASES = [
+    # B, n_q, n_kv, T, d, S, past, theta, layout, scaling
+    (2, 8, 2, 70, 128, 256, [5, 130], 5.0e5, "interleaved", None),
+    (1, 6, 2, 100, 64, 160, [33], 1.0e4, "interleaved", None),       # g = 3: 42 positions per workgroup
+    (2, 4, 4, 65, 128, 200, [0, 64], 5.0e5, "half", None),           # g = 1
+    (1, 32, 2, 40, 128, 100, [27], 5.0e5, "interleaved", SCALED),    # g = 16
+    (3, 16, 2, 1, 128, 300, [299 - 1, 10, 200], 5.0e5, "interleaved", None),  # T = 1
+]
+
+
+def run_prefill_e2e(case, seed):
+    B, n_q, n_kv, T, d, S, past, theta, layout, scaling = case
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed)
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
+    ref = attend(q_ref, kc_ref, vc_ref, past, n_kv)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling)
+    out = gq.gqa_prefill_attn(q_rot, kc_d, vc_d, pl, max(past))
+    torch.cuda.synchronize()
+    return synth.bits(out), ref, (q_rot, kc_d, vc_d, pl)
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}T{c[3]}d{c[4]}")
+def test_prefill_end_to_end(case):
+    say(f"prefill e2e {case[:7]}")
+    got, ref, _ = run_prefill_e2e(case, seed=500 + case[3])
+    check_out(got, ref, "prefill")
+
+
+def test_prefill_split_equals_whole():
+    """prefill(T) == prefill(T-1) then a one-token decode at the next position."""
+    B, n_q, n_kv, T, d, S, past = 2, 32, 8, 33, 128, 200, [40, 100]
+    say("prefill split")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=42)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), 5.0e5)
+    whole = gq.gqa_prefill_attn(q_rot, kc_d, vc_d, pl, max(past))
+    head = gq.gqa_prefill_attn(q_rot[:, :, :T - 1].contiguous(), kc_d, vc_d, pl, max(past))
+    pl_last = past_dev([p + T - 1 for p in past])
+    tail = gq.gqa_decode_attn(q_rot[:, :, T - 1:].contiguous(), kc_d, vc_d, pl_last, max(past) + T - 1)
+    torch.cuda.synchronize()
+    w = bf16_to_f64(synth.bits(whole))
+    check_out(synth.bits(head), w[:, :, :T - 1], "prefill head vs whole")
+    check_out(synth.bits(tail), w[:, :, T - 1:], "decode tail vs whole")
+
+
+# ---------------------------------------------------------------- full-size workloads (sampled outputs)
+
+def full_size_decode(name, sample_b, layer_seed_offset=0):
+    w = synth.WORKLOADS[name]
+    B, n_q, n_kv, d, S = w["B"], w["n_q"], w["n_kv"], w["d"], w["S"]
+    past = synth.past_lengths(B, w["past"], w["seed"])
+    seed = w["seed"] + layer_seed_offset
+    say(f"{name}: B={B} n_q={n_q} n_kv={n_kv} S={S} max past {past.max()}")
+    kc = synth.normal_bf16((B, n_kv, S, d), seed + 3, DEV)
+    vc = synth.normal_bf16((B, n_kv, S, d), seed + 4, DEV)
+    q = synth.normal_bf16((B, n_q, 1, d), seed, DEV)
+    kn = synth.normal_bf16((B, n_kv, 1, d), seed + 1, DEV)
+    vn = synth.normal_bf16((B, n_kv, 1, d), seed + 2, DEV)
+    synth.poison_beyond(kc, past, 1)
+    synth.poison_beyond(vc, past, 1)
+    sb = np.asarray(sample_b)
+    # the oracle sees the sampled sequences' inputs as they are before the step
+    kc_s, vc_s = synth.bits(kc[sb]), synth.bits(vc[sb])
+    q_s, kn_s, vn_s = synth.bits(q[sb]), synth.bits(kn[sb]), synth.bits(vn[sb])
+    pl = past_dev(past)
+    q_rot = gq.gqa_rope_append(q, kn, vn, kc, vc, pl, int(past.max()), w["theta"], "interleaved", w["scaling"])
+    out = gq.gqa_decode_attn(q_rot, kc, vc, pl, int(past.max()))
+    torch.cuda.synchronize()
+    got = synth.bits(out[sb])
+    q_ref, kc_ref, vc_ref = rope_append(q_s, kn_s, vn_s, kc_s, vc_s, past[sb], w["theta"], "interleaved",
+                                        w["scaling"])
+    ref = attend(q_ref, kc_ref, vc_ref, past[sb], n_kv)
+    check_out(got, ref, name)
+    assert max_ulp(synth.bits(q_rot[sb]), q_ref) <= 1
+    for i, b in enumerate(sb):
+        p = int(past[b])
+        assert max_ulp(synth.bits(kc[b, :, p]), kc_ref[i, :, p]) <= 1
+        assert np.array_equal(synth.bits(vc[b, :, p]), vc_ref[i, :, p])
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+def test_full_size_batched_decode_layer():
+    """B=32 ragged contexts up to 8192, one layer of the 32-layer step (sampled sequences)."""
+    full_size_decode("llama8b_b32_decode_32layers", sample_b=[0, 5, 13, 31])
+
+
+def test_full_size_long_context_scaled_decode():
+    """B=64, 64/8 heads, ragged 4096..8191, scaled RoPE: one of the 80 layer calls (sampled)."""
+    full_size_decode("llama70b_shape_decode_scaled", sample_b=[0, 17, 63])
+
+
+def test_full_size_chunked_prefill():
+    w = synth.WORKLOADS["llama8b_chunked_prefill"]
+    B, n_q, n_kv, T, d, S = w["B"], w["n_q"], w["n_kv"], w["T"], w["d"], w["S"]
+    past = synth.past_lengths(B, w["past"], w["seed"])
+    say(f"chunked prefill: B={B} T={T} P={past.tolist()}")
+    seed = w["seed"]
+    kc = synth.normal_bf16((B, n_kv, S, d), seed + 3, DEV)
+    vc = synth.normal_bf16((B, n_kv, S, d), seed + 4, DEV)
+    q = synth.normal_bf16((B, n_q, T, d), seed, DEV)
+    kn = synth.normal_bf16((B, n_kv, T, d), seed + 1, DEV)
+    vn = synth.normal_bf16((B, n_kv, T, d), seed + 2, DEV)
+    synth.poison_beyond(kc, past, T)
+    synth.poison_beyond(vc, past, T)
+    sb = np.array([0, 3])
+    kc_s, vc_s = synth.bits(kc[sb]), synth.bits(vc[sb])
+    q_s, kn_s, vn_s = synth.bits(q[sb]), synth.bits(kn[sb]), synth.bits(vn[sb])
+    pl = past_dev(past)
+    q_rot = gq.gqa_rope_append(q, kn, vn, kc, vc, pl, int(past.max()), w["theta"])
+    out = gq.gqa_prefill_attn(q_rot, kc, vc, pl, int(past.max()))
+    torch.cuda.synchronize()
+    q_ref, kc_ref, vc_ref = rope_append(q_s, kn_s, vn_s, kc_s, vc_s, past[sb], w["theta"])
+    ref = attend(q_ref, kc_ref, vc_ref, past[sb], n_kv)
+    check_out(synth.bits(out[sb]), ref, "chunked prefill")
