@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and 70B-shape figures")
     ap.add_argument("--decode-wg", type=int, default=0, help="override the split-K workgroup count")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="first run one plain device copy of this many GiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -181,6 +183,16 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     gq.gqa_set_decode_workgroups(args.decode_wg)
+
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30))
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: {n} bytes read and {n} bytes written by one copy kernel", file=sys.stderr)
+        del src, dst
+        torch.cuda.empty_cache()
 
     step, info, tensors = decode_workload(gq, synth, HEADLINE, dev)
     print(f"# headline workload ready: B={info['B']} layers={info['layers']} mean ctx "

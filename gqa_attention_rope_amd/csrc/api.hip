@@ -7,7 +7,7 @@
 
 #include <vector>
 
-#include "../../include/gqa.h"
+#include "gqa.h"
 #include "kernels.hpp"
 
 namespace {

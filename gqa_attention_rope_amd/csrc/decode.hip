@@ -16,14 +16,18 @@
 //    is launched idle.  A share may start or end inside a segment; each
 //    (segment, workgroup) piece leaves one partial record per wave and head.
 //  * Inside a workgroup (4 waves) a tile's K and V rows are loaded once from
-//    HBM with 16-byte coalesced loads, staged through registers into LDS, and
-//    the next tile's loads are in flight while the current one is computed.
-//  * Waves split the tile by (head group, row group).  Within a wave, lane
-//    (r = lane/8, e = lane%8) owns 16-byte pieces e and e+8 of a row: q.k is a
-//    v_dot2_f32_bf16 chain over those pieces followed by a DPP reduction over
-//    the 8 lanes of the row.  Online softmax keeps a running max and sum per
-//    head (wave reductions by DPP / lane shuffles), and the weighted value sum
-//    is accumulated by the same lanes over pairs of rows.
+//    HBM with 16-byte coalesced raw buffer loads (the descriptor covers only
+//    the segment's valid rows, so the hardware range check zero-fills the
+//    rest), staged through two register stages into LDS, so the loads of the
+//    next two tiles are in flight while one is computed.
+//  * Waves split the tile by (head group, row group).  For q.k, lane
+//    (r = lane/8, e = lane%8) owns 16-byte pieces e and e+8 of a row: a
+//    v_dot2_f32_bf16 chain over those pieces, then a DPP reduction over the 8
+//    lanes of the row.  Online softmax keeps a running max and sum per head
+//    (wave reductions by DPP / lane shuffles).  The weights go through a small
+//    per-wave LDS buffer, and for the weighted value sum every lane owns d/64
+//    output dims of all the wave's heads, so the accumulator is a few
+//    registers and the kernel fits four workgroups per CU.
 //  * A second kernel merges the records of each (sequence, head) in a fixed
 //    order: M = max m, l = sum l e^(m-M), o = sum o e^(m-M) / l.  No atomics,
 //    so results are bitwise reproducible for a given workgroup count.
@@ -38,13 +42,14 @@ namespace {
 
 constexpr int TILE = 64;
 constexpr int THREADS = 256;
+constexpr int WAVES = THREADS / 64;
 constexpr float LOG2E = 1.4426950408889634f;
 
 template <int D, int HGW, int NHG>
 struct Cfg {
     static constexpr int NP = D / 64;              // 16-byte pieces per lane per row
     static constexpr int PPR = D / 8;              // 16-byte pieces per row
-    static constexpr int RG = 4 / NHG;             // row groups per tile
+    static constexpr int RG = WAVES / NHG;         // row groups per tile
     static constexpr int ROWS_W = TILE / RG;       // rows of a tile one wave handles
     static constexpr int PASSES = ROWS_W / 8;      // q.k passes of 8 rows
     static constexpr int GC = HGW * NHG;           // heads per segment
@@ -53,50 +58,40 @@ struct Cfg {
     static constexpr int LOADS = 2 * TILE * PPR / THREADS;  // 16-byte loads per thread per tile
 };
 
-// LDS position of 16-byte piece c of tile row R.  Rows two apart land in
-// opposite halves of the 64 banks, so the 16 lanes of one LDS access phase
-// never collide.
-template <int PPR>
-__device__ __forceinline__ int lds_pos(int R, int c) {
-    return PPR == 16 ? (R * PPR + (c ^ (((R >> 1) & 1) << 3))) : (R * PPR + c);
-}
-
 __device__ __forceinline__ int tiles_of(const int32_t* past_len, int b, int pmax) {
     int P = past_len[b];
     P = P < 0 ? 0 : (P > pmax ? pmax : P);
     return (P + 1 + TILE - 1) / TILE;  // rows 0..P
 }
 
-// Exclusive prefix of per-sequence tile counts into s_pre[0..B] (B <= DECODE_MAX_B).
+// Exclusive prefix of per-sequence tile counts into s_pre[0..B], 256 sequences
+// per pass with one (clamped, unconditional) load per thread, so every pass
+// costs a single memory round trip.
 __device__ void tile_prefix(const int32_t* past_len, int B, int pmax, int* s_pre, int* s_wsum) {
-    constexpr int PER = DECODE_MAX_B / THREADS;
     const int tid = threadIdx.x;
-    int loc[PER];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int b = tid * PER + i;
-        loc[i] = sum;
-        sum += (b < B) ? tiles_of(past_len, b, pmax) : 0;
-    }
     const int lane = tid & 63, wv = tid >> 6;
-    int x = sum;
+    int carry = 0;
+    for (int base = 0; base < B; base += THREADS) {
+        const int b = base + tid;
+        const int n = tiles_of(past_len, b < B ? b : B - 1, pmax);
+        const int mine = b < B ? n : 0;
+        int x = mine;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) s_wsum[wv] = x;
+        __syncthreads();
+        int before = carry;
+        for (int k = 0; k < wv; ++k) before += s_wsum[k];
+        if (b < B) s_pre[b] = before + x - mine;
+        int total = carry;
+        for (int k = 0; k < THREADS / 64; ++k) total += s_wsum[k];
+        carry = total;
+        __syncthreads();
     }
-    if (lane == 63) s_wsum[wv] = x;
-    __syncthreads();
-    int base = 0;
-    for (int k = 0; k < wv; ++k) base += s_wsum[k];
-    const int excl = base + x - sum;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int b = tid * PER + i;
-        if (b < B) s_pre[b] = excl + loc[i];
-    }
-    if (tid == THREADS - 1) s_pre[B] = excl + sum;
+    if (tid == 0) s_pre[B] = carry;
     __syncthreads();
 }
 
@@ -107,26 +102,48 @@ __device__ __forceinline__ long long owner_of(long long tau, long long T, long l
     return ((tau + 1) * G - 1) / T;
 }
 
+// Position of one tile in the concatenated tile list: sequence b, segment sj
+// (= KV head * head chunks + chunk) inside it, tile tt inside the segment.
+struct Cursor {
+    int b, sj, tt, nt, L;
+};
+
+// Byte offset in the LDS tile of 16-byte piece c of row R (rows of D bf16).
+// For d = 128, rows two apart use opposite halves of the 64 banks (piece
+// index XOR 8), so the 16 lanes of one LDS access phase never collide.
+template <int D>
+__device__ __forceinline__ int lds_byte(int R, int c) {
+    return D == 128 ? R * 256 + ((c ^ (((R >> 1) & 1) << 3)) << 4) : R * 128 + (c << 4);
+}
+
 template <int D, int HGW, int NHG>
 __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ past_len, int pmax, float* __restrict__ ws, int B, int n_q, int n_kv, int S, int nhc,
     float scale_log2) {
     using C = Cfg<D, HGW, NHG>;
-    constexpr int NP = C::NP, PPR = C::PPR, PASSES = C::PASSES;
-    __shared__ uint4 s_k[TILE * PPR];
-    __shared__ uint4 s_v[TILE * PPR];
-    __shared__ int s_pre[DECODE_MAX_B + 1];
+    constexpr int NP = C::NP, PASSES = C::PASSES;
+    constexpr int DPL = D / 64;                  // value dims each lane accumulates
+    constexpr int ROWB = D * 2;                  // bytes per cache row
+    constexpr int TILEB = TILE * ROWB;           // bytes per K (or V) tile
+    constexpr int HALF = C::LOADS / 2;           // 16-byte loads per thread per K (or V) tile
+    __shared__ __align__(16) unsigned char s_kv[2 * TILEB];  // K tile, then V tile
+    __shared__ float4 s_p[THREADS / 64][PASSES][8];          // softmax weights of each wave's rows
+    __shared__ u32x4_t s_q[C::GC * (D / 8)];                  // the segment's GC query rows
     __shared__ int s_wsum[THREADS / 64];
+    extern __shared__ int s_pre[];  // B + 1 entries
 
     tile_prefix(past_len, B, pmax, s_pre, s_wsum);
 
-    const long long segs_per_b = (long long)n_kv * nhc;
-    const long long T_all = segs_per_b * s_pre[B];
+    // values read from LDS are the same in every lane: keep them in scalar registers
+    auto uni = [] __attribute__((always_inline)) (int x) { return __builtin_amdgcn_readfirstlane(x); };
+    const int segs_per_b = n_kv * nhc;
+    const long long T_all = (long long)segs_per_b * uni(s_pre[B]);
     const long long G = gridDim.x, w = blockIdx.x;
-    long long tau = share_begin(w, T_all, G);
+    const long long tau0 = share_begin(w, T_all, G);
     const long long tau_end = share_begin(w + 1, T_all, G);
-    if (tau >= tau_end) return;
+    if (tau0 >= tau_end) return;
+    const int n_tiles = (int)(tau_end - tau0);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -135,136 +152,133 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const int rbase = rg * C::ROWS_W;
     const int g = n_q / n_kv;
 
-    // locate the segment holding the first tile: largest b with segs_per_b*s_pre[b] <= tau
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (segs_per_b * s_pre[mid] <= tau) lo = mid; else hi = mid - 1;
-    }
-    int b = lo;
-    int nt = s_pre[b + 1] - s_pre[b];
-    long long off = tau - segs_per_b * s_pre[b];
-    int sj = (int)(off / nt);   // segment within the sequence: j * nhc + hc
-    int tt = (int)(off % nt);   // tile within the segment
-
-    auto seq_rows = [&](int bb) {
+    auto rows_of = [&] __attribute__((always_inline)) (int bb) {
         int P = past_len[bb];
         P = P < 0 ? 0 : (P > pmax ? pmax : P);
         return P + 1;
     };
-    int L = seq_rows(b);
-
-    // ---- staged tile loads (registers), zero beyond the last valid row
-    uint4 stage[C::LOADS];
-    auto load_tile = [&](int bb, int sjj, int ttt, int LL) {
-        const int j = sjj / nhc;
-        const size_t base = ((size_t)(bb * n_kv + j) * S + (size_t)ttt * TILE) * D;
-        const int valid = LL - ttt * TILE;
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int pi = tid + THREADS * i;
-            const int which = pi / (TILE * PPR);  // 0 = K, 1 = V
-            const int row = (pi / PPR) % TILE;
-            const int c = pi % PPR;
-            const uint16_t* src = (which ? v_cache : k_cache) + base + (size_t)row * D + 8 * c;
-            stage[i] = row < valid ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+    Cursor cur;  // first tile: largest b with segs_per_b * s_pre[b] <= tau0
+    {
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((long long)segs_per_b * uni(s_pre[mid]) <= tau0) lo = mid; else hi = mid - 1;
         }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int pi = tid + THREADS * i;
-            const int which = pi / (TILE * PPR);
-            const int row = (pi / PPR) % TILE;
-            const int c = pi % PPR;
-            (which ? s_v : s_k)[lds_pos<PPR>(row, c)] = stage[i];
+        cur.b = uni(lo);
+        cur.nt = uni(s_pre[cur.b + 1] - s_pre[cur.b]);
+        const long long off = tau0 - (long long)segs_per_b * uni(s_pre[cur.b]);
+        cur.sj = uni((int)(off / cur.nt));
+        cur.tt = uni((int)(off % cur.nt));
+        cur.L = uni(rows_of(cur.b));
+    }
+    auto advance = [&] __attribute__((always_inline)) (Cursor& c) {
+        if (++c.tt < c.nt) return;
+        c.tt = 0;
+        if (++c.sj < segs_per_b) return;
+        c.sj = 0;
+        if (++c.b < B) {
+            c.nt = uni(s_pre[c.b + 1] - s_pre[c.b]);
+            c.L = uni(rows_of(c.b));
         }
     };
 
-    // ---- per-wave softmax state for its HGW heads
-    uint4 qv[HGW][NP];
+    // ---- tile loads: raw buffer loads over the segment's valid rows only.  The
+    // descriptor's range check returns zeros for rows at or beyond L, so the
+    // last partial tile needs no clamping and never touches rows beyond L.
+    // Thread tid loads bytes tid*16 + i*4096 of the tile: 16 consecutive lanes
+    // cover one 256-byte row, fully coalesced.
+    u32x4_t st[C::LOADS];
+    auto load_tile = [&] __attribute__((always_inline)) (const Cursor& c) {
+        const size_t seg_off = (size_t)(c.b * n_kv + c.sj / nhc) * S * D;
+        const int valid_bytes = c.L * ROWB;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg_off), (short)0, valid_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg_off), (short)0, valid_bytes, 0x00020000);
+        const int soff = c.tt * TILEB;
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            st[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + i * THREADS * 16, 0);
+            st[HALF + i] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + i * THREADS * 16, 0);
+        }
+    };
+    // LDS position of the bytes this thread loaded: row tid*16/ROWB + i*(4096/ROWB), piece (tid*16 % ROWB)/16;
+    // the swizzle bit depends only on tid, so every store is base + constant.
+    const int st_base = lds_byte<D>((tid * 16) / ROWB, ((tid * 16) % ROWB) >> 4);
+    auto store_tile = [&] __attribute__((always_inline)) () {
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            *reinterpret_cast<u32x4_t*>(s_kv + st_base + i * THREADS * 16) = st[i];
+            *reinterpret_cast<u32x4_t*>(s_kv + TILEB + st_base + i * THREADS * 16) = st[HALF + i];
+        }
+    };
+
+    // ---- per-wave softmax state for its HGW heads; lane owns value dims DPL*lane ..
     float m_run[HGW], l_run[HGW];
-    float o[HGW][8 * NP];
-    auto reset_state = [&]() {
+    float o[HGW][DPL];
+    auto reset_state = [&] __attribute__((always_inline)) () {
 #pragma unroll
         for (int h = 0; h < HGW; ++h) {
             m_run[h] = -INFINITY;
             l_run[h] = 0.f;
 #pragma unroll
-            for (int x = 0; x < 8 * NP; ++x) o[h][x] = 0.f;
+            for (int x = 0; x < DPL; ++x) o[h][x] = 0.f;
         }
     };
-    auto load_q = [&](int bb, int sjj) {
-        const int j = sjj / nhc, hc = sjj % nhc;
-#pragma unroll
-        for (int h = 0; h < HGW; ++h) {
-            const int hq = j * g + hc * C::GC + hg * HGW + h;
-            const uint4* src = reinterpret_cast<const uint4*>(q_rot + (size_t)(bb * n_q + hq) * D);
-#pragma unroll
-            for (int pp = 0; pp < NP; ++pp) qv[h][pp] = src[e + 8 * pp];
-        }
+    // The segment's GC query rows, one 16-byte piece per thread.  The piece is
+    // loaded together with the segment's first tile (same register stage), so
+    // waiting for that tile's loads also covers it and never drains the
+    // younger prefetches.
+    constexpr int QPIECES = C::GC * (D / 8);
+    auto load_q = [&] __attribute__((always_inline)) (const Cursor& c) -> u32x4_t {
+        const int j = c.sj / nhc, hc = c.sj % nhc;
+        const int piece = tid < QPIECES ? tid : 0;
+        const int hq = j * g + hc * C::GC + piece / (D / 8);
+        return reinterpret_cast<const u32x4_t*>(q_rot + (size_t)(c.b * n_q + hq) * D)[piece % (D / 8)];
     };
-    auto flush = [&](int bb, int sjj) {
-        const long long seg = (long long)bb * segs_per_b + sjj;
+    auto flush = [&] __attribute__((always_inline)) (const Cursor& c) {
+        const long long seg = (long long)c.b * segs_per_b + c.sj;
         float* slot = ws + (size_t)(seg + w) * C::SLOT;
 #pragma unroll
         for (int h = 0; h < HGW; ++h) {
-            const float l_tot = sum_hi3(l_run[h]);
-            float ov[8 * NP];
-#pragma unroll
-            for (int x = 0; x < 8 * NP; ++x) ov[x] = sum_hi3(o[h][x]);
-            if (r == 0) {
-                float* rec = slot + (size_t)(rg * C::GC + hg * HGW + h) * C::REC;
-                if (e == 0) {
-                    rec[0] = m_run[h];
-                    rec[1] = l_tot;
-                }
-#pragma unroll
-                for (int pp = 0; pp < NP; ++pp) {
-                    float4* dst = reinterpret_cast<float4*>(rec + 4 + 8 * (e + 8 * pp));
-                    dst[0] = make_float4(ov[8 * pp + 0], ov[8 * pp + 1], ov[8 * pp + 2], ov[8 * pp + 3]);
-                    dst[1] = make_float4(ov[8 * pp + 4], ov[8 * pp + 5], ov[8 * pp + 6], ov[8 * pp + 7]);
-                }
+            const float l_tot = sum_hi3(l_run[h]);  // l_run is kept per row lane: sum over the 8 row lanes
+            float* rec = slot + (size_t)(rg * C::GC + hg * HGW + h) * C::REC;
+            if (lane == 0) {
+                rec[0] = m_run[h];
+                rec[1] = l_tot;
             }
+            if (DPL == 2)
+                *reinterpret_cast<float2*>(rec + 4 + 2 * lane) = make_float2(o[h][0], o[h][DPL - 1]);
+            else
+                rec[4 + lane] = o[h][0];
         }
     };
 
-    reset_state();
-    load_tile(b, sj, tt, L);
-    bool seg_start = true;
+    // LDS read bases.  q.k: lane (r, e) reads pieces e + 8pp of rows rbase + 2r + const.
+    int qk_base[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) qk_base[pp] = lds_byte<D>(rbase + 2 * r, e + 8 * pp);
+    // value sum: every lane reads its DPL dims of a row; the swizzle depends on the row's parity class.
+    const int pv_base0 = D == 128 ? lds_byte<D>(rbase, lane >> 2) + (lane & 3) * 4 : rbase * ROWB + lane * 2;
+    const int pv_base1 = D == 128 ? lds_byte<D>(rbase + 2, lane >> 2) + (lane & 3) * 4 - 2 * ROWB : pv_base0;
 
-    for (; tau < tau_end; ++tau) {
-        if (seg_start) load_q(b, sj);
-        __syncthreads();  // every wave is done reading the previous tile
-        store_tile();
-        __syncthreads();
-
-        // coordinates of the next tile; issue its loads before computing this one
-        int nb = b, nsj = sj, ntt = tt + 1, nL = L, nnt = nt;
-        if (ntt == nt) {
-            ntt = 0;
-            if (++nsj == (int)segs_per_b) {
-                nsj = 0;
-                ++nb;
-                if (nb < B) {
-                    nnt = s_pre[nb + 1] - s_pre[nb];
-                    nL = seq_rows(nb);
-                }
-            }
-        }
-        const bool more = tau + 1 < tau_end;
-        if (more) load_tile(nb, nsj, ntt, nL);
-
-        // ---- q.k for this wave's rows, HGW heads
-        const int row0 = tt * TILE;
+    // ---- one tile: q.k, online softmax, weighted value sum (this wave's rows and heads)
+    auto compute_tile = [&] __attribute__((always_inline)) (const Cursor& c) {
+        const int row0 = c.tt * TILE;
         float sc[PASSES][HGW];
 #pragma unroll
         for (int k = 0; k < PASSES; ++k) {
-            const int R = rbase + 16 * (k >> 1) + 2 * r + (k & 1);
-            uint4 kp[NP];
+            const int dR = 16 * (k >> 1) + (k & 1);  // row offset of this pass (rows rbase + 2r + dR)
+            u32x4_t kp[NP];
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp) kp[pp] = s_k[lds_pos<PPR>(R, e + 8 * pp)];
-            const bool valid = row0 + R < L;
+            for (int pp = 0; pp < NP; ++pp)
+                kp[pp] = *reinterpret_cast<const u32x4_t*>(s_kv + qk_base[pp] + dR * ROWB);
+            u32x4_t qv[HGW][NP];
+#pragma unroll
+            for (int h = 0; h < HGW; ++h)
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) qv[h][pp] = s_q[(hg * HGW + h) * (D / 8) + e + 8 * pp];
+            const bool valid = row0 + rbase + 2 * r + dR < c.L;
 #pragma unroll
             for (int h = 0; h < HGW; ++h) {
                 float acc = 0.f;
@@ -279,9 +293,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
                 sc[k][h] = valid ? acc * scale_log2 : -INFINITY;
             }
         }
-
-        // ---- online softmax (base-2 exponent, scores already scaled by log2 e)
-        bool rescale = false;
+        // online softmax (base-2 exponent: scores already carry the log2 e factor)
         float alpha[HGW];
 #pragma unroll
         for (int h = 0; h < HGW; ++h) {
@@ -300,67 +312,136 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
                 ps += sc[k][h];
             }
             l_run[h] = l_run[h] * alpha[h] + ps;
-            rescale |= alpha[h] != 1.f;
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) o[h][x] *= alpha[h];
         }
-        if (rescale) {
+        // weights to LDS (one lane per row), then every lane sums its value dims over the rows
+        if (e == 0) {
 #pragma unroll
-            for (int h = 0; h < HGW; ++h)
+            for (int k = 0; k < PASSES; ++k) {
+                float pv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int x = 0; x < 8 * NP; ++x) o[h][x] *= alpha[h];
+                for (int h = 0; h < HGW; ++h) pv[h] = sc[k][h];
+                s_p[wave][k][r] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+            }
         }
-
-        // ---- weighted value sum over row pairs (rows of passes 2m and 2m+1)
+        __builtin_amdgcn_wave_barrier();
+        const unsigned char* vt = s_kv + TILEB;
 #pragma unroll
-        for (int mm = 0; mm < NHG; ++mm) {
-            const int R0 = rbase + 16 * mm + 2 * r;
+        for (int k = 0; k < PASSES; ++k) {
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp) {
-                const uint4 v0 = s_v[lds_pos<PPR>(R0, e + 8 * pp)];
-                const uint4 v1 = s_v[lds_pos<PPR>(R0 + 1, e + 8 * pp)];
-                const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w};
-                const uint32_t c[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float a0 = bf_lo(a[x]), a1 = bf_hi(a[x]);
-                    const float c0 = bf_lo(c[x]), c1 = bf_hi(c[x]);
+            for (int rr = 0; rr < 8; ++rr) {
+                const int dR = 16 * (k >> 1) + 2 * rr + (k & 1);  // row rbase + dR; parity class of dR>>1 is rr&1
+                const float4 p4 = s_p[wave][k][rr];
+                const float pw[4] = {p4.x, p4.y, p4.z, p4.w};
+                if (DPL == 2) {
+                    const uint32_t vw =
+                        *reinterpret_cast<const uint32_t*>(vt + ((rr & 1) ? pv_base1 : pv_base0) + dR * ROWB);
+                    const float v0 = bf_lo(vw), v1 = bf_hi(vw);
 #pragma unroll
                     for (int h = 0; h < HGW; ++h) {
-                        const float p0 = sc[2 * mm][h], p1 = sc[2 * mm + 1][h];
-                        o[h][8 * pp + 2 * x] += p0 * a0 + p1 * c0;
-                        o[h][8 * pp + 2 * x + 1] += p0 * a1 + p1 * c1;
+                        o[h][0] += pw[h] * v0;
+                        o[h][DPL - 1] += pw[h] * v1;
                     }
+                } else {
+                    const uint32_t vh = *reinterpret_cast<const uint16_t*>(vt + pv_base0 + dR * ROWB);
+                    const float v0 = __uint_as_float(vh << 16);
+#pragma unroll
+                    for (int h = 0; h < HGW; ++h) o[h][0] += pw[h] * v0;
+                }
+                // keep at most two rows' LDS reads in flight: the empty asm pins the
+                // accumulators here, so the sums above cannot sink below later reads
+                if (rr & 1) {
+#pragma unroll
+                    for (int h = 0; h < HGW; ++h)
+#pragma unroll
+                        for (int x = 0; x < DPL; ++x) asm volatile("" : "+v"(o[h][x]));
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
+        __builtin_amdgcn_wave_barrier();
+    };
 
-        const bool seg_end = !more || nb != b || nsj != sj;
+    // ---- main loop: two register stages, so the next two tiles' loads are in
+    // flight while one is computed from LDS.  Every step issues the same loads
+    // on every path (past the end of the share it re-reads the current tile,
+    // and it always fetches the q piece of the tile's segment), so the count
+    // of outstanding loads is path-independent and each wait drains only the
+    // stage it needs.
+    u32x4_t st2[C::LOADS];
+    Cursor ld = cur;  // next tile to load
+    u32x4_t q2 = load_q(ld);
+    load_tile(ld);
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) st2[i] = st[i];
+    if (n_tiles > 1) advance(ld);
+    u32x4_t q1 = load_q(ld);
+    load_tile(ld);  // into st: st2 holds the first tile, st the second
+    if (n_tiles > 2) advance(ld);
+    reset_state();
+    bool seg_start = true;
+    auto step = [&] __attribute__((always_inline)) (u32x4_t (&buf)[C::LOADS], u32x4_t& qbuf, int i) {
+        __syncthreads();  // every wave is done with the previous tile in LDS
+#pragma unroll
+        for (int x = 0; x < HALF; ++x) {
+            *reinterpret_cast<u32x4_t*>(s_kv + st_base + x * THREADS * 16) = buf[x];
+            *reinterpret_cast<u32x4_t*>(s_kv + TILEB + st_base + x * THREADS * 16) = buf[HALF + x];
+        }
+        if (seg_start && tid < QPIECES) s_q[tid] = qbuf;
+        __syncthreads();
+        {
+            // loads of tile i+2 (or, past the end, the last tile again) into the stage just drained
+            const size_t seg_off = (size_t)(ld.b * n_kv + ld.sj / nhc) * S * D;
+            const int valid_bytes = ld.L * ROWB;
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg_off), (short)0, valid_bytes, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg_off), (short)0, valid_bytes, 0x00020000);
+            const int soff = ld.tt * TILEB;
+#pragma unroll
+            for (int x = 0; x < HALF; ++x) {
+                buf[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + x * THREADS * 16, 0);
+                buf[HALF + x] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + x * THREADS * 16, 0);
+            }
+            qbuf = load_q(ld);
+            if (i + 3 < n_tiles) advance(ld);
+        }
+        compute_tile(cur);
+        Cursor nx = cur;
+        advance(nx);
+        const bool seg_end = i + 1 == n_tiles || nx.b != cur.b || nx.sj != cur.sj;
         if (seg_end) {
-            flush(b, sj);
+            flush(cur);
             reset_state();
         }
         seg_start = seg_end;
-        b = nb;
-        sj = nsj;
-        tt = ntt;
-        L = nL;
-        nt = nnt;
+        cur = nx;
+    };
+    int i = 0;
+    for (; i + 1 < n_tiles; i += 2) {  // straight-line pairs: no path-dependent load counts
+        step(st2, q2, i);
+        step(st, q1, i + 1);
     }
+    if (i < n_tiles) step(st2, q2, i);
 }
 
-// Merge of the partial records of one (sequence, query head).
+// Merge of the partial records of one (sequence, query head), in a fixed
+// order.  Lane i first reads the (max, sum) of record i; the output sum then
+// walks the records in batches of 8 whose loads are all in flight together.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws,
                                                             const int32_t* __restrict__ past_len, int pmax,
                                                             uint16_t* __restrict__ out, int B, int n_q, int n_kv,
                                                             int nhc, int gc, int rg_count, int slot_floats, int G) {
     constexpr int DPL = D / 64;  // dims per lane
+    constexpr int REC = D + 4;
     const int h = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x;
     const int g = n_q / n_kv;
 
     // prefix of tile counts (same clamping as the partial kernel)
     long long pre_b = 0, total = 0;
-    int nt_b = 0;
     for (int base = 0; base < B; base += 64) {
         const int bb = base + lane;
         const int n = bb < B ? tiles_of(past_len, bb, pmax) : 0;
@@ -374,7 +455,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
         pre_b += before;
         total += all;
     }
-    nt_b = tiles_of(past_len, b, pmax);
+    const int nt_b = tiles_of(past_len, b, pmax);
 
     const int j = h / g, hh = h % g, hc = hh / gc, hl = hh % gc;
     const long long segs_per_b = (long long)n_kv * nhc;
@@ -383,32 +464,63 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     const long long start = segs_per_b * pre_b + (long long)(j * nhc + hc) * nt_b;
     const long long end = start + nt_b;
     const long long w_lo = owner_of(start, T_all, G), w_hi = owner_of(end - 1, T_all, G);
+    const int nrec = (int)(w_hi - w_lo + 1) * rg_count;
+
+    auto rec_ptr = [&](int idx) -> const float* {
+        const long long w = w_lo + idx / rg_count;
+        return ws + (size_t)(seg + w) * slot_floats + (size_t)((idx % rg_count) * gc + hl) * REC;
+    };
+    auto live = [&](int idx) {  // the workgroup of this record had a non-empty share
+        const long long w = w_lo + idx / rg_count;
+        return share_begin(w, T_all, G) < share_begin(w + 1, T_all, G);
+    };
 
     float M = -INFINITY;
-    for (long long w = w_lo; w <= w_hi; ++w) {
-        const long long s0 = share_begin(w, T_all, G), s1 = share_begin(w + 1, T_all, G);
-        if (s0 >= s1) continue;
-        const float* slot = ws + (size_t)(seg + w) * slot_floats;
-        for (int rg = 0; rg < rg_count; ++rg) M = fmaxf(M, slot[(size_t)(rg * gc + hl) * (D + 4)]);
+    for (int base = 0; base < nrec; base += 64) {
+        const int idx = base + lane;
+        if (idx < nrec && live(idx)) M = fmaxf(M, rec_ptr(idx)[0]);
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+
     float acc[DPL];
 #pragma unroll
     for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-    float lsum = 0.f;
-    for (long long w = w_lo; w <= w_hi; ++w) {
-        const long long s0 = share_begin(w, T_all, G), s1 = share_begin(w + 1, T_all, G);
-        if (s0 >= s1) continue;
-        const float* slot = ws + (size_t)(seg + w) * slot_floats;
-        for (int rg = 0; rg < rg_count; ++rg) {
-            const float* rec = slot + (size_t)(rg * gc + hl) * (D + 4);
-            const float m = rec[0];
-            const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-            lsum += f * rec[1];
+    float lpart = 0.f;
+    for (int base = 0; base < nrec; base += 64) {
+        const int idx = base + lane;
+        float f = 0.f;
+        if (idx < nrec && live(idx)) {
+            const float* rp = rec_ptr(idx);
+            const float m = rp[0];
+            f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+            lpart += f * rp[1];
+        }
+        const int cnt = (nrec - base) < 64 ? (nrec - base) : 64;
+        for (int i = 0; i < cnt; i += 8) {
+            float fb[8];
+            float ob[8][DPL];
 #pragma unroll
-            for (int x = 0; x < DPL; ++x) acc[x] += f * rec[4 + DPL * lane + x];
+            for (int k = 0; k < 8; ++k) {
+                fb[k] = (i + k < cnt) ? __shfl(f, i + k, 64) : 0.f;
+#pragma unroll
+                for (int x = 0; x < DPL; ++x) ob[k][x] = 0.f;
+                if (fb[k] != 0.f) {
+                    const float* rp = rec_ptr(base + i + k) + 4 + DPL * lane;
+#pragma unroll
+                    for (int x = 0; x < DPL; ++x) ob[k][x] = rp[x];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int x = 0; x < DPL; ++x) acc[x] += fb[k] * ob[k][x];
         }
     }
-    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
+
+    const float inv = 1.f / lpart;
     uint16_t* dst = out + (size_t)(b * n_q + h) * D + DPL * lane;
     if (DPL == 2) {
         *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[DPL - 1] * inv);
@@ -421,23 +533,24 @@ template <int D, int HGW, int NHG>
 hipError_t launch_partial_t(int G, const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                             const int32_t* past_len, int pmax, float* ws, int B, int n_q, int n_kv, int S, int nhc,
                             float scale_log2, hipStream_t st) {
-    hipLaunchKernelGGL((decode_partial_kernel<D, HGW, NHG>), dim3(G), dim3(THREADS), 0, st, q_rot, k_cache, v_cache,
-                       past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2);
+    const size_t dyn = (size_t)(B + 1) * sizeof(int);
+    hipLaunchKernelGGL((decode_partial_kernel<D, HGW, NHG>), dim3(G), dim3(THREADS), dyn, st, q_rot, k_cache,
+                       v_cache, past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2);
     return hipGetLastError();
 }
 
 template <int D, int HGW, int NHG>
-int occupancy_t() {
+int occupancy_t(int B) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_partial_kernel<D, HGW, NHG>, THREADS, 0) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_partial_kernel<D, HGW, NHG>, THREADS,
+                                                     (size_t)(B + 1) * sizeof(int)) != hipSuccess)
         return 1;
     return blocks > 0 ? blocks : 1;
 }
 
+using occ_fn = int (*)(int);
 using partial_fn = hipError_t (*)(int, const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int, float*,
                                   int, int, int, int, int, float, hipStream_t);
-using occ_fn = int (*)();
 
 struct Variant {
     int hgw, nhg;
@@ -470,7 +583,7 @@ DecodePlan decode_plan(int n_q, int n_kv, int d) {
     p.nhg = v.nhg;
     p.gc = v.hgw * v.nhg;
     p.nhc = g / p.gc;
-    p.rg = 4 / v.nhg;
+    p.rg = WAVES / v.nhg;
     p.rec = d + 4;
     p.slot_floats = (size_t)p.rg * p.gc * p.rec;
     return p;
@@ -498,7 +611,11 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
         if (e != hipSuccess) return e;
     }
     int G = wg_override;
-    if (G <= 0) G = cu_count * (d == 128 ? v.occ128() : v.occ64());
+    // default: as many workgroups as fit on the chip at once (one wave of workgroups)
+    if (G <= 0) {
+        const int bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
+        G = cu_count * (d == 128 ? v.occ128(bs) : v.occ64(bs));
+    }
     if (G > DECODE_MAX_WG) G = DECODE_MAX_WG;
     if (G < 1) G = 1;
     const float scale_log2 = scale * LOG2E;
