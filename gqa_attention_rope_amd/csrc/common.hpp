@@ -62,12 +62,31 @@ __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// v + (v moved by DPP CTRL); bound_ctrl zero-fills lanes without a source, so
+// the compiler can fold the move into the add (v_add_f32 with a DPP operand)
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
 // sum over the 8 lanes of each aligned group of 8 (all 8 lanes receive it)
 __device__ __forceinline__ float sum8(float v) {
-    v += dpp_f32<0xB1>(v);
-    v += dpp_f32<0x4E>(v);
-    v += dpp_f32<0x141>(v);
+    v = add_dpp<0xB1>(v);
+    v = add_dpp<0x4E>(v);
+    v = add_dpp<0x141>(v);
     return v;
+}
+
+// maximum over lane bits 3, 4 and 5 (the 8 row groups of 8 lanes, values
+// replicated inside each group), returned wave-uniform: row_ror:8 pairs the two
+// groups of each 16-lane row, row_bcast:15 and row_bcast:31 carry the running
+// maximum into rows 1..3, and lane 63 ends up with the maximum of all.
+__device__ __forceinline__ float max_rows_uniform(float v) {
+    const int ninf = (int)0xff800000u;
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x142, 0xa, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x143, 0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float xor_f32(float v, int mask) { return __shfl_xor(v, mask, 64); }

@@ -42,6 +42,7 @@ namespace {
 
 constexpr int TILE = 64;
 constexpr int THREADS = 256;
+constexpr int PARK = 2;  // finished pieces a workgroup keeps in LDS until its share is done
 constexpr int WAVES = THREADS / 64;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -131,6 +132,12 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     __shared__ float4 s_p[THREADS / 64][PASSES][8];          // softmax weights of each wave's rows
     __shared__ u32x4_t s_q[C::GC * (D / 8)];                  // the segment's GC query rows
     __shared__ int s_wsum[THREADS / 64];
+    // Finished pieces are parked here (each wave in its own region) and
+    // written to the workspace after the loop: global stores inside the loop
+    // share the in-order load counter with the tile prefetches, and every
+    // wait for a tile would also wait for their completion.
+    __shared__ float s_park[PARK][THREADS / 64][HGW][D + 12];  // o[D], l per row lane [D, D+8), m at D+8
+    __shared__ int s_park_seg[PARK];
     extern __shared__ int s_pre[];  // B + 1 entries
 
     tile_prefix(past_len, B, pmax, s_pre, s_wsum);
@@ -236,21 +243,46 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         const int hq = j * g + hc * C::GC + piece / (D / 8);
         return reinterpret_cast<const u32x4_t*>(q_rot + (size_t)(c.b * n_q + hq) * D)[piece % (D / 8)];
     };
-    auto flush = [&] __attribute__((always_inline)) (const Cursor& c) {
-        const long long seg = (long long)c.b * segs_per_b + c.sj;
+    // write one finished piece's records straight to the workspace (used past
+    // the parking capacity, and after the loop for the parked pieces)
+    auto write_records = [&] __attribute__((always_inline)) (long long seg, const float* m4, const float* l4,
+                                                             const float (*o4)[DPL]) {
         float* slot = ws + (size_t)(seg + w) * C::SLOT;
 #pragma unroll
         for (int h = 0; h < HGW; ++h) {
-            const float l_tot = sum_hi3(l_run[h]);  // l_run is kept per row lane: sum over the 8 row lanes
             float* rec = slot + (size_t)(rg * C::GC + hg * HGW + h) * C::REC;
             if (lane == 0) {
-                rec[0] = m_run[h];
-                rec[1] = l_tot;
+                rec[0] = m4[h];
+                rec[1] = l4[h];
             }
             if (DPL == 2)
-                *reinterpret_cast<float2*>(rec + 4 + 2 * lane) = make_float2(o[h][0], o[h][DPL - 1]);
+                *reinterpret_cast<float2*>(rec + 4 + 2 * lane) = make_float2(o4[h][0], o4[h][DPL - 1]);
             else
-                rec[4 + lane] = o[h][0];
+                rec[4 + lane] = o4[h][0];
+        }
+    };
+    int n_parked = 0;
+    auto flush = [&] __attribute__((always_inline)) (const Cursor& c) {
+        const long long seg = (long long)c.b * segs_per_b + c.sj;
+        if (n_parked < PARK) {
+            // wave-private LDS: o, m, and the 8 per-row-lane partial sums of l
+#pragma unroll
+            for (int h = 0; h < HGW; ++h) {
+                float* pk = s_park[n_parked][wave][h];
+                if (DPL == 2)
+                    *reinterpret_cast<float2*>(pk + 2 * lane) = make_float2(o[h][0], o[h][DPL - 1]);
+                else
+                    pk[lane] = o[h][0];
+                if (e == 0) pk[D + r] = l_run[h];
+                if (lane == 0) pk[D + 8] = m_run[h];
+            }
+            if (tid == 0) s_park_seg[n_parked] = (int)seg;
+            ++n_parked;
+        } else {
+            float l4[HGW];
+#pragma unroll
+            for (int h = 0; h < HGW; ++h) l4[h] = sum_hi3(l_run[h]);
+            write_records(seg, m_run, l4, o);
         }
     };
 
@@ -424,6 +456,24 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         step(st, q1, i + 1);
     }
     if (i < n_tiles) step(st2, q2, i);
+
+    // records of the parked pieces
+    __syncthreads();
+    for (int pk = 0; pk < n_parked; ++pk) {
+        float m4[HGW], l4[HGW], o4[HGW][DPL];
+#pragma unroll
+        for (int h = 0; h < HGW; ++h) {
+            const float* src = s_park[pk][wave][h];
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) o4[h][x] = src[DPL * lane + x];
+            float l = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) l += src[D + k];
+            l4[h] = l;
+            m4[h] = src[D + 8];
+        }
+        write_records(s_park_seg[pk], m4, l4, o4);
+    }
 }
 
 // Merge of the partial records of one (sequence, query head), in a fixed
