@@ -11,7 +11,10 @@ Printed: one JSON line.  value = KV-read GB/s over the whole step
 (sum over layers and sequences of (past_len+1) * n_kv * d * 2 tensors * 2 B,
 divided by the step time); tokens/s = B / step time.  roofline = the decode
 split-K kernel's algorithmic bytes per launch over its average launch time
-(HIP events on the launch stream), against 8 TB/s.  cpu_baseline = the fp64
+(HIP events on the launch stream), against 8 TB/s; roofline.traffic = HBM bytes
+per launch from the committed rocprofv3 byte-counter summary under profiles/
+(null once the decode kernel sources differ from the ones it was taken on).
+cpu_baseline = the fp64
 oracle on a bounded sample of the same workload, on this host.
 """
 
@@ -28,6 +31,36 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HEADLINE = "llama8b_b32_decode_32layers"
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "decode_partial_llama8b_b32_decode_32layers_hbm_counters.txt")
+KERNEL_SOURCES = ("gqa_attention_rope_amd/csrc/decode.hip", "gqa_attention_rope_amd/csrc/common.hpp",
+                  "gqa_attention_rope_amd/csrc/kernels.hpp", "gqa_attention_rope_amd/build.py")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per decode split-K launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    each counter scaled by its plain-copy calibration factor.  None when the kernel sources have changed
+    since the counters were taken (or the summary is absent)."""
+    try:
+        with open(COUNTERS) as fh:
+            rec = next(json.loads(l[len("RECORD "):]) for l in fh if l.startswith("RECORD "))
+    except (OSError, StopIteration, ValueError):
+        return None, "no counter summary"
+    if rec.get("source_sha256_16") != kernel_source_hash():
+        return None, "decode kernel sources changed since the counters were taken"
+    t = rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]
+    return int(round(t)), "rocprofv3 FETCH_SIZE x%g + WRITE_SIZE x%g (plain-copy calibration), bytes per launch" % (
+        rec["fetch_factor"], rec["write_factor"])
 
 
 def parse():
@@ -205,8 +238,11 @@ def main():
     avg_ms, per_kind = kernel_avg(gq, step, max(5, args.steps // 5), "decode_partial")
     alg = info["kv_per_layer"] + info["q_bytes"]
     achieved = alg / (avg_ms * 1e-3) / 1e9
+    traffic, traffic_note = counter_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_note": traffic_note,
+                "traffic_over_alg": round(traffic / alg, 4) if traffic else None,
                 "kernel": "decode_partial_kernel<128,4,1>", "avg_launch_us": round(avg_ms * 1e3, 2),
                 "alg_bytes_per_launch": alg}
     kinds = {k: {"avg_us": round(v[0] / max(v[1], 1) * 1e3, 2), "launches": v[1]} for k, v in per_kind.items() if v[1]}
