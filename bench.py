@@ -132,7 +132,7 @@ def decode_workload(gq, synth, name, dev):
     out = torch.empty_like(q)
     pl = torch.as_tensor(past, device=dev)
     maxp = int(past.max())
-    ws = torch.empty(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=dev)
 
     def step():
         for l in range(layers):

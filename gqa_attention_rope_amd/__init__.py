@@ -34,6 +34,7 @@ EXPORTED = (
     "gqa_profile_read",
     "gqa_profile_reset",
     "gqa_set_decode_workgroups",
+    "gqa_set_decode_schedule",
 )
 
 KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3}
@@ -89,6 +90,8 @@ def lib():
     L.gqa_profile_reset.restype = i32
     L.gqa_set_decode_workgroups.argtypes = [i32]
     L.gqa_set_decode_workgroups.restype = i32
+    L.gqa_set_decode_schedule.argtypes = [i32, i32]
+    L.gqa_set_decode_schedule.restype = i32
     _lib = L
     return L
 
@@ -200,7 +203,8 @@ def gqa_decode_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, w
     _bf16(out, "out", (B, n_q, 1, d))
     need = gqa_decode_workspace_bytes(B, n_q, n_kv, d, S)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_rot.device)
+        # the scheduling header at the start must be zero before first use
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q_rot.device)
     _check(lib().gqa_decode_attn(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
                                  _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B, n_q,
                                  n_kv, d, S, float(scale), _stream(stream)))
@@ -243,3 +247,8 @@ def gqa_profile_read(kind):
 
 def gqa_set_decode_workgroups(n):
     return int(lib().gqa_set_decode_workgroups(int(n)))
+
+
+def gqa_set_decode_schedule(static_permille=-1, chunk_tiles=0):
+    """Static fraction (per mille) and dynamic chunk size of the decode split; (-1, 0) = defaults."""
+    _check(lib().gqa_set_decode_schedule(int(static_permille), int(chunk_tiles)))

@@ -213,4 +213,14 @@ int gqa_set_decode_workgroups(int n) {
     return g_decode_wg;
 }
 
+int gqa_set_decode_schedule(int static_permille, int chunk_tiles) {
+    if (static_permille < 0 && chunk_tiles <= 0) {
+        gqa::set_decode_schedule(gqa::DECODE_DEFAULT_STATIC_PM, gqa::DECODE_DEFAULT_CHUNK);
+        return GQA_OK;
+    }
+    if (static_permille < 0 || static_permille > 1000 || chunk_tiles < 1) return GQA_ERR_INVALID_ARG;
+    gqa::set_decode_schedule(static_permille, chunk_tiles);
+    return GQA_OK;
+}
+
 }  // extern "C"

@@ -11,6 +11,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // native 16-byte vector (first-class in LLVM, unlike HIP's uint4 struct)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 

@@ -10,16 +10,29 @@
 // group share each K/V row they read):
 //
 //  * Work unit: a tile of 64 cache rows of one (sequence, KV head, head chunk)
-//    segment.  All tiles of all segments are laid end to end and every
-//    workgroup takes one contiguous, equal share of that list (stream-K
-//    style), so ragged past lengths cost nothing in balance and no workgroup
-//    is launched idle.  A share may start or end inside a segment; each
-//    (segment, workgroup) piece leaves one partial record per wave and head.
+//    segment.  All tiles of all segments are laid end to end.  The first part
+//    of that list (a fixed fraction) is cut into one contiguous, equal share
+//    per workgroup (stream-K style); the rest is cut into small fixed chunks
+//    that workgroups take from a shared ticket counter as they run out of
+//    work.  Workgroups resident on one CU do not progress at the same rate
+//    (instruction issue favours the oldest waves, and the first loads of the
+//    later ones queue behind the earlier ones), so equal static shares alone
+//    leave the slowest workgroup finishing long after the mean; the dynamic
+//    tail absorbs that spread.  Which chunk a ticket names is fixed, so the
+//    records, and the result, do not depend on which workgroup ran it.
+//  * A piece is the part of one segment inside one share or chunk; it leaves
+//    one (max, sum, unnormalised output) record per query head, merged across
+//    the waves of the workgroup through LDS.
 //  * Inside a workgroup (4 waves) a tile's K and V rows are loaded once from
 //    HBM with 16-byte coalesced raw buffer loads (the descriptor covers only
 //    the segment's valid rows, so the hardware range check zero-fills the
 //    rest), staged through two register stages into LDS, so the loads of the
 //    next two tiles are in flight while one is computed.
+//  * Every step issues the same sequence of vector memory instructions: the
+//    record store of the previous piece, the ticket atomic and the loads.  When
+//    one of them has nothing to do its buffer descriptor has a zero range, so
+//    the hardware drops it.  With a path-independent count, every wait for a
+//    stage drains exactly that stage and never the younger prefetches.
 //  * Waves split the tile by (head group, row group).  For q.k, lane
 //    (r = lane/8, e = lane%8) owns 16-byte pieces e and e+8 of a row: a
 //    v_dot2_f32_bf16 chain over those pieces, then a DPP reduction over the 8
@@ -27,10 +40,11 @@
 //    (wave reductions by DPP / lane shuffles).  The weights go through a small
 //    per-wave LDS buffer, and for the weighted value sum every lane owns d/64
 //    output dims of all the wave's heads, so the accumulator is a few
-//    registers and the kernel fits four workgroups per CU.
+//    registers.
 //  * A second kernel merges the records of each (sequence, head) in a fixed
-//    order: M = max m, l = sum l e^(m-M), o = sum o e^(m-M) / l.  No atomics,
-//    so results are bitwise reproducible for a given workgroup count.
+//    order: M = max m, l = sum l e^(m-M), o = sum o e^(m-M) / l, and clears
+//    the ticket counter for the next call.  Results are bitwise reproducible
+//    for a given launch shape.
 #include <float.h>
 
 #include "common.hpp"
@@ -42,9 +56,13 @@ namespace {
 
 constexpr int TILE = 64;
 constexpr int THREADS = 256;
-constexpr int PARK = 2;  // finished pieces a workgroup keeps in LDS until its share is done
 constexpr int WAVES = THREADS / 64;
 constexpr float LOG2E = 1.4426950408889634f;
+// The workspace starts with a 256-byte scheduling header (the ticket counter
+// at offset 0); the records follow.
+constexpr int HDR_FLOATS = 64;
+constexpr uint32_t RSRC_FLAGS = 0x00020000u;  // raw buffer, 32-bit dwords
+constexpr int OOB = 0x7ffffff0;               // a buffer offset past any range: the access is dropped
 
 template <int D, int HGW, int NHG>
 struct Cfg {
@@ -55,7 +73,7 @@ struct Cfg {
     static constexpr int PASSES = ROWS_W / 8;      // q.k passes of 8 rows
     static constexpr int GC = HGW * NHG;           // heads per segment
     static constexpr int REC = D + 4;              // m, l, 2 pad, o[D]
-    static constexpr int SLOT = RG * GC * REC;     // floats per (segment, workgroup) piece
+    static constexpr int SLOT = GC * REC;          // floats per piece (one merged record per head)
     static constexpr int LOADS = 2 * TILE * PPR / THREADS;  // 16-byte loads per thread per tile
 };
 
@@ -117,11 +135,36 @@ __device__ __forceinline__ int lds_byte(int R, int c) {
     return D == 128 ? R * 256 + ((c ^ (((R >> 1) & 1) << 3)) << 4) : R * 128 + (c << 4);
 }
 
+// Tile schedule shared by the partial and combine kernels: tiles [0, Ts) are
+// split into equal contiguous shares, tiles [Ts, T_all) into chunks of C.
+// Tile counts fit in 32 bits: at most 2048 sequences x n_q segments x S/64 tiles.
+struct Sched {
+    int T_all, Ts, n_dyn, C;
+};
+__device__ __forceinline__ Sched make_sched(int T_all, int static_pm, int chunk) {
+    Sched s;
+    s.T_all = T_all;
+    s.Ts = (int)((long long)T_all * static_pm / 1000);
+    s.C = chunk;
+    s.n_dyn = (T_all - s.Ts + chunk - 1) / chunk;
+    return s;
+}
+
+// What one register stage holds (the same in every lane).
+struct Stage {
+    int tt, L;   // tile index inside its segment, valid rows of the segment
+    int slot;    // record slot of the piece the tile belongs to
+    int flags;   // kind (TILE, BUBBLE = nothing loaded but work to come, END) | PIECE_END | GRABBED
+};
+constexpr int K_TILE = 0, K_BUBBLE = 1, K_END = 2, KIND_MASK = 3;
+constexpr int F_PIECE_END = 4;  // last tile of its segment or of its range
+constexpr int F_GRABBED = 8;    // this stage's atomic took a ticket
+
 template <int D, int HGW, int NHG>
 __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ past_len, int pmax, float* __restrict__ ws, int B, int n_q, int n_kv, int S, int nhc,
-    float scale_log2) {
+    float scale_log2, int static_pm, int chunk) {
     using C = Cfg<D, HGW, NHG>;
     constexpr int NP = C::NP, PASSES = C::PASSES;
     constexpr int DPL = D / 64;                  // value dims each lane accumulates
@@ -132,12 +175,9 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     __shared__ float4 s_p[THREADS / 64][PASSES][8];          // softmax weights of each wave's rows
     __shared__ u32x4_t s_q[C::GC * (D / 8)];                  // the segment's GC query rows
     __shared__ int s_wsum[THREADS / 64];
-    // Finished pieces are parked here (each wave in its own region) and
-    // written to the workspace after the loop: global stores inside the loop
-    // share the in-order load counter with the tile prefetches, and every
-    // wait for a tile would also wait for their completion.
-    __shared__ float s_park[PARK][THREADS / 64][HGW][D + 12];  // o[D], l per row lane [D, D+8), m at D+8
-    __shared__ int s_park_seg[PARK];
+    // state of each wave when a piece ends: o[D], m at D, l at D+1
+    __shared__ float s_park[WAVES][HGW][D + 4];
+    __shared__ int s_ticket;
     extern __shared__ int s_pre[];  // B + 1 entries
 
     tile_prefix(past_len, B, pmax, s_pre, s_wsum);
@@ -145,12 +185,12 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     // values read from LDS are the same in every lane: keep them in scalar registers
     auto uni = [] __attribute__((always_inline)) (int x) { return __builtin_amdgcn_readfirstlane(x); };
     const int segs_per_b = n_kv * nhc;
-    const long long T_all = (long long)segs_per_b * uni(s_pre[B]);
-    const long long G = gridDim.x, w = blockIdx.x;
-    const long long tau0 = share_begin(w, T_all, G);
-    const long long tau_end = share_begin(w + 1, T_all, G);
-    if (tau0 >= tau_end) return;
-    const int n_tiles = (int)(tau_end - tau0);
+    const int n_segs = B * segs_per_b;
+    const Sched sc = make_sched(segs_per_b * uni(s_pre[B]), static_pm, chunk);
+    const int G = gridDim.x, w = blockIdx.x;
+    const int dyn_slot0 = n_segs + G;  // slot of chunk t's piece in segment s: dyn_slot0 + t + s
+    int* const ticket_ctr = reinterpret_cast<int*>(ws);
+    float* const recs = ws + HDR_FLOATS;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -164,20 +204,22 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         P = P < 0 ? 0 : (P > pmax ? pmax : P);
         return P + 1;
     };
-    Cursor cur;  // first tile: largest b with segs_per_b * s_pre[b] <= tau0
-    {
+    // cursor of global tile tau: largest b with segs_per_b * s_pre[b] <= tau
+    auto cursor_at = [&] __attribute__((always_inline)) (int tau) {
         int lo = 0, hi = B - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if ((long long)segs_per_b * uni(s_pre[mid]) <= tau0) lo = mid; else hi = mid - 1;
+            if (segs_per_b * uni(s_pre[mid]) <= tau) lo = mid; else hi = mid - 1;
         }
-        cur.b = uni(lo);
-        cur.nt = uni(s_pre[cur.b + 1] - s_pre[cur.b]);
-        const long long off = tau0 - (long long)segs_per_b * uni(s_pre[cur.b]);
-        cur.sj = uni((int)(off / cur.nt));
-        cur.tt = uni((int)(off % cur.nt));
-        cur.L = uni(rows_of(cur.b));
-    }
+        Cursor c;
+        c.b = uni(lo);
+        c.nt = uni(s_pre[c.b + 1] - s_pre[c.b]);
+        const int off = tau - segs_per_b * uni(s_pre[c.b]);
+        c.sj = uni(off / c.nt);
+        c.tt = uni(off % c.nt);
+        c.L = uni(rows_of(c.b));
+        return c;
+    };
     auto advance = [&] __attribute__((always_inline)) (Cursor& c) {
         if (++c.tt < c.nt) return;
         c.tt = 0;
@@ -189,36 +231,90 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         }
     };
 
-    // ---- tile loads: raw buffer loads over the segment's valid rows only.  The
-    // descriptor's range check returns zeros for rows at or beyond L, so the
-    // last partial tile needs no clamping and never touches rows beyond L.
-    // Thread tid loads bytes tid*16 + i*4096 of the tile: 16 consecutive lanes
-    // cover one 256-byte row, fully coalesced.
-    u32x4_t st[C::LOADS];
-    auto load_tile = [&] __attribute__((always_inline)) (const Cursor& c) {
-        const size_t seg_off = (size_t)(c.b * n_kv + c.sj / nhc) * S * D;
-        const int valid_bytes = c.L * ROWB;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg_off), (short)0, valid_bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg_off), (short)0, valid_bytes, 0x00020000);
-        const int soff = c.tt * TILEB;
-#pragma unroll
-        for (int i = 0; i < HALF; ++i) {
-            st[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + i * THREADS * 16, 0);
-            st[HALF + i] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + i * THREADS * 16, 0);
+    // ---- loader: the current range (static share first, then chunks) and at
+    // most one ticket in flight or in hand
+    Cursor ld;
+    ld.b = 0; ld.sj = 0; ld.tt = 0; ld.nt = 1; ld.L = 1;
+    const int tau_w = (int)share_begin(w, sc.Ts, G);
+    int ld_left = (int)share_begin(w + 1, sc.Ts, G) - tau_w;
+    int ld_rid = w;
+    if (ld_left > 0) ld = cursor_at(tau_w);
+    int nx_tau = 0, nx_len = 0, nx_rid = 0;
+    bool have_next = false, no_more = false, pending = false;
+    auto take_ticket = [&] __attribute__((always_inline)) (int t) {
+        if (t >= 0 && t < sc.n_dyn) {  // (a counter left non-zero by a broken caller only loses work)
+            have_next = true;
+            nx_tau = sc.Ts + t * sc.C;
+            nx_len = (sc.T_all - nx_tau) < sc.C ? (sc.T_all - nx_tau) : sc.C;
+            nx_rid = dyn_slot0 + t;
+        } else {
+            no_more = true;
         }
     };
+    // a short share needs the first chunk before the pipeline is primed
+    if (ld_left <= 2) {
+        if (tid == 0) s_ticket = atomicAdd(ticket_ctr, 1);
+        __syncthreads();
+        take_ticket(uni(s_ticket));
+        __syncthreads();
+    }
+
+    // The q piece of a tile's segment, one 16-byte piece per thread (the
+    // segment's GC query rows); the descriptor is empty when nothing is loaded.
+    constexpr int QPIECES = C::GC * (D / 8);
+    // Issue one stage: the ticket atomic, the K/V tile loads and the q piece.
+    auto issue = [&] __attribute__((always_inline)) (u32x4_t (&buf)[C::LOADS], u32x4_t& qbuf, int& tkbuf,
+                                                      Stage& stg) {
+        if (ld_left == 0 && have_next) {
+            ld = cursor_at(nx_tau);
+            ld_left = nx_len;
+            ld_rid = nx_rid;
+            have_next = false;
+        }
+        const bool tile = ld_left > 0;
+        const int rem = tile ? ld_left - 1 : 0;
+        const bool grab = !no_more && !have_next && !pending && rem <= 2;
+        stg.tt = uni(ld.tt);
+        stg.L = uni(ld.L);
+        stg.slot = uni(ld_rid + ld.b * segs_per_b + ld.sj);
+        stg.flags = uni((tile ? K_TILE : ((no_more && !pending) ? K_END : K_BUBBLE)) |
+                        ((ld_left == 1 || ld.tt + 1 == ld.nt) ? F_PIECE_END : 0) | (grab ? F_GRABBED : 0));
+        if (grab) pending = true;
+        // Descriptor fields must be wave-uniform (scalar registers); readfirstlane
+        // states that for values the compiler cannot prove uniform through the loop.
+        // ticket: only lane 0 of wave 0 is inside the 4-byte range, and only when grabbing
+        const __amdgpu_buffer_rsrc_t rt =
+            __builtin_amdgcn_make_buffer_rsrc((void*)ticket_ctr, (short)0, uni(grab ? 4 : 0), RSRC_FLAGS);
+        tkbuf = __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, rt, tid == 0 ? 0 : OOB, 0, 0);
+        // K/V rows of the tile; thread tid loads bytes tid*16 + x*4096 of each
+        const size_t seg_off = (size_t)uni(ld.b * n_kv + ld.sj / nhc) * S * D;
+        const int valid_bytes = uni(tile ? ld.L * ROWB : 0);
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg_off), (short)0, valid_bytes, RSRC_FLAGS);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg_off), (short)0, valid_bytes, RSRC_FLAGS);
+        const int soff = uni(ld.tt * TILEB);
+#pragma unroll
+        for (int x = 0; x < HALF; ++x) {
+            buf[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + x * THREADS * 16, 0);
+            buf[HALF + x] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + x * THREADS * 16, 0);
+        }
+        {
+            const int j = ld.sj / nhc, hc = ld.sj % nhc;
+            const uint16_t* qseg = q_rot + (size_t)uni(ld.b * n_q + j * g + hc * C::GC) * D;
+            const __amdgpu_buffer_rsrc_t rq =
+                __builtin_amdgcn_make_buffer_rsrc((void*)qseg, (short)0, uni(tile ? QPIECES * 16 : 0), RSRC_FLAGS);
+            qbuf = __builtin_amdgcn_raw_buffer_load_b128(rq, tid < QPIECES ? tid * 16 : OOB, 0, 0);
+        }
+        if (tile) {
+            advance(ld);
+            --ld_left;
+        }
+    };
+
     // LDS position of the bytes this thread loaded: row tid*16/ROWB + i*(4096/ROWB), piece (tid*16 % ROWB)/16;
     // the swizzle bit depends only on tid, so every store is base + constant.
     const int st_base = lds_byte<D>((tid * 16) / ROWB, ((tid * 16) % ROWB) >> 4);
-    auto store_tile = [&] __attribute__((always_inline)) () {
-#pragma unroll
-        for (int i = 0; i < HALF; ++i) {
-            *reinterpret_cast<u32x4_t*>(s_kv + st_base + i * THREADS * 16) = st[i];
-            *reinterpret_cast<u32x4_t*>(s_kv + TILEB + st_base + i * THREADS * 16) = st[HALF + i];
-        }
-    };
 
     // ---- per-wave softmax state for its HGW heads; lane owns value dims DPL*lane ..
     float m_run[HGW], l_run[HGW];
@@ -232,57 +328,71 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
             for (int x = 0; x < DPL; ++x) o[h][x] = 0.f;
         }
     };
-    // The segment's GC query rows, one 16-byte piece per thread.  The piece is
-    // loaded together with the segment's first tile (same register stage), so
-    // waiting for that tile's loads also covers it and never drains the
-    // younger prefetches.
-    constexpr int QPIECES = C::GC * (D / 8);
-    auto load_q = [&] __attribute__((always_inline)) (const Cursor& c) -> u32x4_t {
-        const int j = c.sj / nhc, hc = c.sj % nhc;
-        const int piece = tid < QPIECES ? tid : 0;
-        const int hq = j * g + hc * C::GC + piece / (D / 8);
-        return reinterpret_cast<const u32x4_t*>(q_rot + (size_t)(c.b * n_q + hq) * D)[piece % (D / 8)];
-    };
-    // write one finished piece's records straight to the workspace (used past
-    // the parking capacity, and after the loop for the parked pieces)
-    auto write_records = [&] __attribute__((always_inline)) (long long seg, const float* m4, const float* l4,
-                                                             const float (*o4)[DPL]) {
-        float* slot = ws + (size_t)(seg + w) * C::SLOT;
+    auto park = [&] __attribute__((always_inline)) () {
 #pragma unroll
         for (int h = 0; h < HGW; ++h) {
-            float* rec = slot + (size_t)(rg * C::GC + hg * HGW + h) * C::REC;
-            if (lane == 0) {
-                rec[0] = m4[h];
-                rec[1] = l4[h];
-            }
+            float* pk = s_park[wave][h];
             if (DPL == 2)
-                *reinterpret_cast<float2*>(rec + 4 + 2 * lane) = make_float2(o4[h][0], o4[h][DPL - 1]);
+                *reinterpret_cast<float2*>(pk + 2 * lane) = make_float2(o[h][0], o[h][DPL - 1]);
             else
-                rec[4 + lane] = o4[h][0];
+                pk[lane] = o[h][0];
+            const float l = sum_hi3(l_run[h]);
+            if (lane == 0) *reinterpret_cast<float2*>(pk + D) = make_float2(m_run[h], l);
         }
     };
-    int n_parked = 0;
-    auto flush = [&] __attribute__((always_inline)) (const Cursor& c) {
-        const long long seg = (long long)c.b * segs_per_b + c.sj;
-        if (n_parked < PARK) {
-            // wave-private LDS: o, m, and the 8 per-row-lane partial sums of l
+    // Merge the parked wave states of the finished piece into one record per
+    // head and store it.  The stores are issued on every call; with
+    // valid == false the descriptor range is zero and they are dropped.
+    constexpr int OPAIRS = C::GC * D / 2;
+    constexpr int OITER = (OPAIRS + THREADS - 1) / THREADS;
+    auto merge_weights = [&] __attribute__((always_inline)) (int hh, float (&f)[C::RG], float& M) {
+        const int hgx = hh / HGW, hx = hh % HGW;
+        M = -INFINITY;
 #pragma unroll
-            for (int h = 0; h < HGW; ++h) {
-                float* pk = s_park[n_parked][wave][h];
-                if (DPL == 2)
-                    *reinterpret_cast<float2*>(pk + 2 * lane) = make_float2(o[h][0], o[h][DPL - 1]);
-                else
-                    pk[lane] = o[h][0];
-                if (e == 0) pk[D + r] = l_run[h];
-                if (lane == 0) pk[D + 8] = m_run[h];
+        for (int k = 0; k < C::RG; ++k) M = fmaxf(M, s_park[hgx * C::RG + k][hx][D]);
+#pragma unroll
+        for (int k = 0; k < C::RG; ++k) {
+            const float m = s_park[hgx * C::RG + k][hx][D];
+            f[k] = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+        }
+    };
+    auto store_record = [&] __attribute__((always_inline)) (bool valid, int slot) {
+        const __amdgpu_buffer_rsrc_t rr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(recs + (size_t)uni(valid ? slot : 0) * C::SLOT), (short)0,
+                                              uni(valid ? C::SLOT * 4 : 0), RSRC_FLAGS);
+#pragma unroll
+        for (int k = 0; k < OITER; ++k) {
+            const int p = tid + THREADS * k;
+            const bool in = p < OPAIRS;
+            const int hh = in ? (2 * p) / D : 0, x = (2 * p) % D;
+            float2 v = make_float2(0.f, 0.f);
+            if (valid && in) {
+                float f[C::RG], M;
+                merge_weights(hh, f, M);
+#pragma unroll
+                for (int kk = 0; kk < C::RG; ++kk) {
+                    const float2 ov =
+                        *reinterpret_cast<const float2*>(&s_park[(hh / HGW) * C::RG + kk][hh % HGW][x]);
+                    v.x += f[kk] * ov.x;
+                    v.y += f[kk] * ov.y;
+                }
             }
-            if (tid == 0) s_park_seg[n_parked] = (int)seg;
-            ++n_parked;
-        } else {
-            float l4[HGW];
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rr,
+                                                  in ? (hh * C::REC + 4 + x) * 4 : OOB, 0, 0);
+        }
+        {
+            const bool in = tid < C::GC;
+            float2 v = make_float2(-INFINITY, 0.f);
+            if (valid && in) {
+                float f[C::RG], M;
+                merge_weights(tid, f, M);
+                float l = 0.f;
 #pragma unroll
-            for (int h = 0; h < HGW; ++h) l4[h] = sum_hi3(l_run[h]);
-            write_records(seg, m_run, l4, o);
+                for (int kk = 0; kk < C::RG; ++kk) l += f[kk] * s_park[(tid / HGW) * C::RG + kk][tid % HGW][D + 1];
+                v = make_float2(M, l);
+            }
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), rr, in ? tid * C::REC * 4 : OOB,
+                                                  0, 0);
         }
     };
 
@@ -295,8 +405,8 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const int pv_base1 = D == 128 ? lds_byte<D>(rbase + 2, lane >> 2) + (lane & 3) * 4 - 2 * ROWB : pv_base0;
 
     // ---- one tile: q.k, online softmax, weighted value sum (this wave's rows and heads)
-    auto compute_tile = [&] __attribute__((always_inline)) (const Cursor& c) {
-        const int row0 = c.tt * TILE;
+    auto compute_tile = [&] __attribute__((always_inline)) (int c_tt, int c_L) {
+        const int row0 = c_tt * TILE;
         float sc[PASSES][HGW];
 #pragma unroll
         for (int k = 0; k < PASSES; ++k) {
@@ -310,7 +420,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
             for (int h = 0; h < HGW; ++h)
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp) qv[h][pp] = s_q[(hg * HGW + h) * (D / 8) + e + 8 * pp];
-            const bool valid = row0 + rbase + 2 * r + dR < c.L;
+            const bool valid = row0 + rbase + 2 * r + dR < c_L;
 #pragma unroll
             for (int h = 0; h < HGW; ++h) {
                 float acc = 0.f;
@@ -396,99 +506,85 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     };
 
     // ---- main loop: two register stages, so the next two tiles' loads are in
-    // flight while one is computed from LDS.  Every step issues the same loads
-    // on every path (past the end of the share it re-reads the current tile,
-    // and it always fetches the q piece of the tile's segment), so the count
-    // of outstanding loads is path-independent and each wait drains only the
-    // stage it needs.
-    u32x4_t st2[C::LOADS];
-    Cursor ld = cur;  // next tile to load
-    u32x4_t q2 = load_q(ld);
-    load_tile(ld);
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) st2[i] = st[i];
-    if (n_tiles > 1) advance(ld);
-    u32x4_t q1 = load_q(ld);
-    load_tile(ld);  // into st: st2 holds the first tile, st the second
-    if (n_tiles > 2) advance(ld);
+    // flight while one is computed from LDS.  The prologue issues each stage
+    // exactly as a step does (record stores first), so the counts of
+    // outstanding loads on loop entry equal those on the back edge.
+    u32x4_t st[C::LOADS], st2[C::LOADS];
+    u32x4_t q1, q2;
+    int tk1, tk2;
+    Stage sA, sB;
+    store_record(false, 0);
+    issue(st2, q2, tk2, sA);
+    store_record(false, 0);
+    issue(st, q1, tk1, sB);
     reset_state();
-    bool seg_start = true;
-    auto step = [&] __attribute__((always_inline)) (u32x4_t (&buf)[C::LOADS], u32x4_t& qbuf, int i) {
-        __syncthreads();  // every wave is done with the previous tile in LDS
+    bool seg_start = true;  // the next tile computed starts a piece: its q rows go to LDS
+    bool pend = false;      // a finished piece waits in s_park for its record store
+    int pend_slot = 0;
+    auto step = [&] __attribute__((always_inline)) (u32x4_t (&buf)[C::LOADS], u32x4_t& qbuf, int& tkbuf,
+                                                     Stage& stg) {
+        const Stage cs = stg;
+        __syncthreads();  // every wave is done with the previous tile in LDS and has parked its state
+        store_record(pend, pend_slot);
+        pend = false;
 #pragma unroll
         for (int x = 0; x < HALF; ++x) {
             *reinterpret_cast<u32x4_t*>(s_kv + st_base + x * THREADS * 16) = buf[x];
             *reinterpret_cast<u32x4_t*>(s_kv + TILEB + st_base + x * THREADS * 16) = buf[HALF + x];
         }
         if (seg_start && tid < QPIECES) s_q[tid] = qbuf;
+        if ((cs.flags & F_GRABBED) && tid == 0) s_ticket = tkbuf;
         __syncthreads();
-        {
-            // loads of tile i+2 (or, past the end, the last tile again) into the stage just drained
-            const size_t seg_off = (size_t)(ld.b * n_kv + ld.sj / nhc) * S * D;
-            const int valid_bytes = ld.L * ROWB;
-            const __amdgpu_buffer_rsrc_t rk =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg_off), (short)0, valid_bytes, 0x00020000);
-            const __amdgpu_buffer_rsrc_t rv =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg_off), (short)0, valid_bytes, 0x00020000);
-            const int soff = ld.tt * TILEB;
-#pragma unroll
-            for (int x = 0; x < HALF; ++x) {
-                buf[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + x * THREADS * 16, 0);
-                buf[HALF + x] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + x * THREADS * 16, 0);
+        if (cs.flags & F_GRABBED) {
+            take_ticket(uni(s_ticket));
+            pending = false;
+        }
+        issue(buf, qbuf, tkbuf, stg);
+        if ((cs.flags & KIND_MASK) == K_TILE) {
+            compute_tile(cs.tt, cs.L);
+            seg_start = (cs.flags & F_PIECE_END) != 0;
+            if (seg_start) {
+                park();
+                reset_state();
+                pend = true;
+                pend_slot = cs.slot;
             }
-            qbuf = load_q(ld);
-            if (i + 3 < n_tiles) advance(ld);
         }
-        compute_tile(cur);
-        Cursor nx = cur;
-        advance(nx);
-        const bool seg_end = i + 1 == n_tiles || nx.b != cur.b || nx.sj != cur.sj;
-        if (seg_end) {
-            flush(cur);
-            reset_state();
-        }
-        seg_start = seg_end;
-        cur = nx;
     };
-    int i = 0;
-    for (; i + 1 < n_tiles; i += 2) {  // straight-line pairs: no path-dependent load counts
-        step(st2, q2, i);
-        step(st, q1, i + 1);
+    // Stages end in order (once one is END all later ones are), so a single
+    // exit at the bottom suffices: stage A is never END at the top, and a step
+    // on an END stage (possible for B) only stores the pending record.  One
+    // exit keeps every path into the loop head issuing the same loads.
+    if ((sA.flags & KIND_MASK) != K_END) {
+        do {
+            step(st2, q2, tk2, sA);
+            step(st, q1, tk1, sB);
+        } while ((sA.flags & KIND_MASK) != K_END);
     }
-    if (i < n_tiles) step(st2, q2, i);
-
-    // records of the parked pieces
     __syncthreads();
-    for (int pk = 0; pk < n_parked; ++pk) {
-        float m4[HGW], l4[HGW], o4[HGW][DPL];
-#pragma unroll
-        for (int h = 0; h < HGW; ++h) {
-            const float* src = s_park[pk][wave][h];
-#pragma unroll
-            for (int x = 0; x < DPL; ++x) o4[h][x] = src[DPL * lane + x];
-            float l = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) l += src[D + k];
-            l4[h] = l;
-            m4[h] = src[D + 8];
-        }
-        write_records(s_park_seg[pk], m4, l4, o4);
-    }
+    store_record(pend, pend_slot);
 }
 
 // Merge of the partial records of one (sequence, query head), in a fixed
-// order.  Lane i first reads the (max, sum) of record i; the output sum then
-// walks the records in batches of 8 whose loads are all in flight together.
+// order: the static shares that hold tiles of the head's segment, in
+// workgroup order, then its chunks in chunk order.  Records are taken in
+// batches of 16 whose loads are all in flight together, and merged online
+// (running max, rescaled sum and output).  Block (0, 0) also clears the ticket
+// counter, so the next call starts from zero.
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws,
+__global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ ws,
                                                             const int32_t* __restrict__ past_len, int pmax,
                                                             uint16_t* __restrict__ out, int B, int n_q, int n_kv,
-                                                            int nhc, int gc, int rg_count, int slot_floats, int G) {
+                                                            int nhc, int gc, int G, int static_pm, int chunk) {
     constexpr int DPL = D / 64;  // dims per lane
     constexpr int REC = D + 4;
+    constexpr int RB = 16;       // records per batch
     const int h = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x;
     const int g = n_q / n_kv;
+    if (h == 0 && b == 0 && lane == 0) reinterpret_cast<int*>(ws)[0] = 0;
+    const float* recs = ws + HDR_FLOATS;
+    const size_t slot_floats = (size_t)gc * REC;
 
     // prefix of tile counts (same clamping as the partial kernel)
     long long pre_b = 0, total = 0;
@@ -509,68 +605,70 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 
     const int j = h / g, hh = h % g, hc = hh / gc, hl = hh % gc;
     const long long segs_per_b = (long long)n_kv * nhc;
-    const long long T_all = segs_per_b * total;
+    const long long n_segs = (long long)B * segs_per_b;
+    const Sched sc = make_sched((int)(segs_per_b * total), static_pm, chunk);
     const long long seg = (long long)b * segs_per_b + (long long)j * nhc + hc;
     const long long start = segs_per_b * pre_b + (long long)(j * nhc + hc) * nt_b;
     const long long end = start + nt_b;
-    const long long w_lo = owner_of(start, T_all, G), w_hi = owner_of(end - 1, T_all, G);
-    const int nrec = (int)(w_hi - w_lo + 1) * rg_count;
-
-    auto rec_ptr = [&](int idx) -> const float* {
-        const long long w = w_lo + idx / rg_count;
-        return ws + (size_t)(seg + w) * slot_floats + (size_t)((idx % rg_count) * gc + hl) * REC;
-    };
-    auto live = [&](int idx) {  // the workgroup of this record had a non-empty share
-        const long long w = w_lo + idx / rg_count;
-        return share_begin(w, T_all, G) < share_begin(w + 1, T_all, G);
-    };
-
-    float M = -INFINITY;
-    for (int base = 0; base < nrec; base += 64) {
-        const int idx = base + lane;
-        if (idx < nrec && live(idx)) M = fmaxf(M, rec_ptr(idx)[0]);
+    // static shares: candidate workgroups w_lo..w_lo + n_st - 1 (some may hold no tile)
+    const long long s_end = end < sc.Ts ? end : sc.Ts;
+    long long w_lo = 0, n_st = 0;
+    if (start < s_end) {
+        w_lo = owner_of(start, sc.Ts, G);
+        n_st = owner_of(s_end - 1, sc.Ts, G) - w_lo + 1;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    // chunks t_lo..t_lo + n_dy - 1
+    const long long d_start = start > sc.Ts ? start : sc.Ts;
+    long long t_lo = 0, n_dy = 0;
+    if (d_start < end) {
+        t_lo = (d_start - sc.Ts) / sc.C;
+        n_dy = (end - 1 - sc.Ts) / sc.C - t_lo + 1;
+    }
+    const int nrec = (int)(n_st + n_dy);
+    const long long dyn_slot0 = n_segs + G;
 
-    float acc[DPL];
+    // record idx is used if it exists and (static) its workgroup had a non-empty share;
+    // record 0 always exists, so unused entries read it and are ignored
+    auto slot_of = [&](int idx, bool& use) -> long long {
+        use = idx < nrec;
+        if (!use) idx = 0;
+        if (idx < n_st) {
+            const long long w = w_lo + idx;
+            use = use && share_begin(w, sc.Ts, G) < share_begin(w + 1, sc.Ts, G);
+            return w + seg;
+        }
+        return dyn_slot0 + t_lo + (idx - n_st) + seg;
+    };
+
+    float M = -INFINITY, L = 0.f, acc[DPL];
 #pragma unroll
     for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-    float lpart = 0.f;
-    for (int base = 0; base < nrec; base += 64) {
-        const int idx = base + lane;
-        float f = 0.f;
-        if (idx < nrec && live(idx)) {
-            const float* rp = rec_ptr(idx);
-            const float m = rp[0];
-            f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-            lpart += f * rp[1];
+    for (int base = 0; base < nrec; base += RB) {
+        float2 ml[RB];
+        float ov[RB][DPL];
+        bool use[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+            const float* rp = recs + (size_t)slot_of(base + u, use[u]) * slot_floats + (size_t)hl * REC;
+            ml[u] = *reinterpret_cast<const float2*>(rp);
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) ov[u][x] = rp[4 + DPL * lane + x];
         }
-        const int cnt = (nrec - base) < 64 ? (nrec - base) : 64;
-        for (int i = 0; i < cnt; i += 8) {
-            float fb[8];
-            float ob[8][DPL];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                fb[k] = (i + k < cnt) ? __shfl(f, i + k, 64) : 0.f;
+        for (int u = 0; u < RB; ++u) {
+            const float m = ml[u].x;
+            if (!use[u] || m == -INFINITY) continue;
+            const float mn = fmaxf(M, m);
+            const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);
+            const float f = fast_exp2(m - mn);
+            L = L * a + f * ml[u].y;
 #pragma unroll
-                for (int x = 0; x < DPL; ++x) ob[k][x] = 0.f;
-                if (fb[k] != 0.f) {
-                    const float* rp = rec_ptr(base + i + k) + 4 + DPL * lane;
-#pragma unroll
-                    for (int x = 0; x < DPL; ++x) ob[k][x] = rp[x];
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-#pragma unroll
-                for (int x = 0; x < DPL; ++x) acc[x] += fb[k] * ob[k][x];
+            for (int x = 0; x < DPL; ++x) acc[x] = acc[x] * a + f * ov[u][x];
+            M = mn;
         }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lpart += __shfl_xor(lpart, off, 64);
 
-    const float inv = 1.f / lpart;
+    const float inv = 1.f / L;
     uint16_t* dst = out + (size_t)(b * n_q + h) * D + DPL * lane;
     if (DPL == 2) {
         *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[DPL - 1] * inv);
@@ -582,10 +680,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 template <int D, int HGW, int NHG>
 hipError_t launch_partial_t(int G, const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                             const int32_t* past_len, int pmax, float* ws, int B, int n_q, int n_kv, int S, int nhc,
-                            float scale_log2, hipStream_t st) {
+                            float scale_log2, int static_pm, int chunk, hipStream_t st) {
     const size_t dyn = (size_t)(B + 1) * sizeof(int);
     hipLaunchKernelGGL((decode_partial_kernel<D, HGW, NHG>), dim3(G), dim3(THREADS), dyn, st, q_rot, k_cache,
-                       v_cache, past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2);
+                       v_cache, past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2, static_pm, chunk);
     return hipGetLastError();
 }
 
@@ -600,7 +698,7 @@ int occupancy_t(int B) {
 
 using occ_fn = int (*)(int);
 using partial_fn = hipError_t (*)(int, const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int, float*,
-                                  int, int, int, int, int, float, hipStream_t);
+                                  int, int, int, int, int, float, int, int, hipStream_t);
 
 struct Variant {
     int hgw, nhg;
@@ -623,7 +721,15 @@ const Variant& pick_variant(int g) {
     return kVariants[sizeof(kVariants) / sizeof(kVariants[0]) - 1];
 }
 
+int g_static_pm = DECODE_DEFAULT_STATIC_PM;
+int g_chunk = DECODE_DEFAULT_CHUNK;
+
 }  // namespace
+
+void set_decode_schedule(int static_permille, int chunk_tiles) {
+    g_static_pm = static_permille;
+    g_chunk = chunk_tiles;
+}
 
 DecodePlan decode_plan(int n_q, int n_kv, int d) {
     const int g = n_q / n_kv;
@@ -635,7 +741,7 @@ DecodePlan decode_plan(int n_q, int n_kv, int d) {
     p.nhc = g / p.gc;
     p.rg = WAVES / v.nhg;
     p.rec = d + 4;
-    p.slot_floats = (size_t)p.rg * p.gc * p.rec;
+    p.slot_floats = (size_t)p.gc * p.rec;
     return p;
 }
 
@@ -643,7 +749,9 @@ size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d) {
     const DecodePlan p = decode_plan(n_q, n_kv, d);
     const int bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
     const size_t segs = (size_t)bs * n_kv * p.nhc;
-    return (segs + DECODE_MAX_WG) * p.slot_floats * sizeof(float);
+    // static pieces: segment + workgroup < segs + G; chunk pieces: segs + G + chunk + segment
+    const size_t slots = 2 * segs + DECODE_MAX_WG + DECODE_MAX_CHUNKS;
+    return (HDR_FLOATS + slots * p.slot_floats) * sizeof(float);
 }
 
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -669,6 +777,7 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
     if (G > DECODE_MAX_WG) G = DECODE_MAX_WG;
     if (G < 1) G = 1;
     const float scale_log2 = scale * LOG2E;
+    const int spm = g_static_pm;
 
     for (int b0 = 0; b0 < B; b0 += DECODE_MAX_B) {
         const int nb = (B - b0) < DECODE_MAX_B ? (B - b0) : DECODE_MAX_B;
@@ -678,19 +787,27 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
         const int32_t* pl = past_len + b0;
         uint16_t* o = out + (size_t)b0 * n_q * d;
 
+        // chunk size: the requested one, grown if the dynamic part could need
+        // more than DECODE_MAX_CHUNKS chunks (bounded with every past_len at max_past_len)
+        const long long t_max = (long long)nb * n_kv * p.nhc * ((max_past_len + 1 + TILE - 1) / TILE);
+        const long long t_dyn = t_max - t_max * spm / 1000;
+        long long chunk = g_chunk;
+        const long long need = (t_dyn + DECODE_MAX_CHUNKS - 1) / DECODE_MAX_CHUNKS;
+        if (chunk < need) chunk = need;
+
         prof_begin(K_DECODE_PARTIAL, st);
         hipError_t e = (d == 128 ? v.fn128 : v.fn64)(G, q, kc, vc, pl, max_past_len, ws, nb, n_q, n_kv, S, p.nhc,
-                                                     scale_log2, st);
+                                                     scale_log2, spm, (int)chunk, st);
         prof_end(K_DECODE_PARTIAL, st);
         if (e != hipSuccess) return e;
 
         prof_begin(K_DECODE_COMBINE, st);
         if (d == 128)
             hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64), 0, st, ws, pl, max_past_len, o,
-                               nb, n_q, n_kv, p.nhc, p.gc, p.rg, (int)p.slot_floats, G);
+                               nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk);
         else
             hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64), 0, st, ws, pl, max_past_len, o,
-                               nb, n_q, n_kv, p.nhc, p.gc, p.rg, (int)p.slot_floats, G);
+                               nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk);
         prof_end(K_DECODE_COMBINE, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

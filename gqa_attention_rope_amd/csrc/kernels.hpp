@@ -33,6 +33,13 @@ hipError_t launch_rope_append(const uint16_t* q, uint16_t* q_rot, const uint16_t
 constexpr int DECODE_MAX_B = 2048;
 // Upper bound on the number of split-K workgroups (sizes the workspace).
 constexpr int DECODE_MAX_WG = 2048;
+// Work schedule of the split-K kernel: this many per-mille of the tiles are
+// split into equal static shares, the rest into chunks of DECODE_DEFAULT_CHUNK
+// tiles handed out by a ticket counter (at most DECODE_MAX_CHUNKS chunks; the
+// chunk grows when a launch would need more).
+constexpr int DECODE_DEFAULT_STATIC_PM = 700;
+constexpr int DECODE_DEFAULT_CHUNK = 3;
+constexpr int DECODE_MAX_CHUNKS = 8192;
 
 struct DecodePlan {
     int hgw;   // query heads per wave (1..4)
@@ -41,10 +48,11 @@ struct DecodePlan {
     int nhc;   // segments per (sequence, KV head) = g / gc
     int rg;    // row groups per workgroup = 4 / nhg
     int rec;   // floats per partial record = d + 4
-    size_t slot_floats;  // rg * gc * rec
+    size_t slot_floats;  // gc * rec: one record per head of a piece
 };
 DecodePlan decode_plan(int n_q, int n_kv, int d);
 size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d);
+void set_decode_schedule(int static_permille, int chunk_tiles);
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
                          int n_kv, int d, int S, float scale, int wg_override, hipStream_t st);

@@ -7,11 +7,13 @@
 // the rotated keys and the values are written at rows past_len .. past_len+T-1
 // and nothing else in the cache changes.
 //
-// One workgroup handles one token (t, b): it computes the d/2 angles of its
-// position once, in fp64, keeps cos/sin in LDS, and then every thread turns
-// 8 pairs at a time (two 16-byte loads, two 16-byte stores) over all n_q query
-// heads and n_kv key heads, and copies the value rows.  All global accesses
-// are 16-byte and contiguous along d.
+// A token (t, b) is covered by one or more workgroups of 256 threads; each
+// thread owns one item: 8 pairs of one head of q or of the new k (two 16-byte
+// loads, two 16-byte stores), or 16 values of a v row (copied).  Each
+// workgroup computes the d/2 angles of the token's position in fp64 and keeps
+// cos/sin in LDS; the item loads are issued before that, since the source rows
+// do not depend on past_len.  All global accesses are 16-byte and contiguous
+// along d.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,6 +52,10 @@ __device__ __forceinline__ void turn(float a, float b, double c, double s, uint3
     rb = f64_to_bf16_rne(da * s + db * c);
 }
 
+// One workgroup covers up to 256 items of one token (t, b); an item is 8 pairs
+// of one head (two 16-byte pieces), of q, of the new k, or of v (copied).  The
+// source rows do not depend on past_len, so each thread issues its loads
+// first; the angles are computed while they are in flight.
 template <int D>
 __global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uint16_t* q_rot,
                                                           const uint16_t* __restrict__ k_new,
@@ -66,9 +72,32 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uin
     const int t = blockIdx.x;
     const int b = blockIdx.y;
     const int P = past_len[b];
+    const int heads = n_q + 2 * n_kv;
+    const int it = blockIdx.z * blockDim.x + threadIdx.x;
+    const bool active = it < heads * ITEMS_PER_HEAD;
+    const int head = active ? it / ITEMS_PER_HEAD : 0;
+    const int c = it % ITEMS_PER_HEAD;
+    const bool is_v = head >= n_q + n_kv, is_k = !is_v && head >= n_q;
+    // two 16-byte pieces: 8 (a, b) pairs, or 16 values of v
+    const uint16_t* src;
+    int off0, off1;
+    if (is_v) {
+        src = v_new + ((size_t)(b * n_kv + head - n_q - n_kv) * T + t) * D;
+        off0 = 16 * c;
+        off1 = 16 * c + 8;
+    } else {
+        src = is_k ? k_new + ((size_t)(b * n_kv + head - n_q) * T + t) * D : q + ((size_t)(b * n_q + head) * T + t) * D;
+        off0 = rp.layout == 0 ? 16 * c : 8 * c;
+        off1 = rp.layout == 0 ? 16 * c + 8 : HALF + 8 * c;
+    }
+    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
+    if (active) {
+        x0 = *reinterpret_cast<const uint4*>(src + off0);
+        x1 = *reinterpret_cast<const uint4*>(src + off1);
+    }
+
     if (P < 0 || P > max_past_len) return;  // caller error: write nothing for this sequence
     const int pos = P + t;                  // < max_past_len + T <= S (checked on the host)
-
     for (int i = threadIdx.x; i < HALF; i += blockDim.x) {
         double ang = (double)pos * pair_frequency(i, D, rp);
         double sn, cs;
@@ -77,62 +106,42 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uin
         s_sin[i] = sn;
     }
     __syncthreads();
+    if (!active) return;
 
-    const int heads = n_q + 2 * n_kv;
-    const int items = heads * ITEMS_PER_HEAD;
-    for (int it = threadIdx.x; it < items; it += blockDim.x) {
-        const int head = it / ITEMS_PER_HEAD;
-        const int c = it % ITEMS_PER_HEAD;
-        if (head >= n_q + n_kv) {  // value row: bit copy of 16 values
-            const int j = head - n_q - n_kv;
-            const uint4* src = reinterpret_cast<const uint4*>(v_new + ((size_t)(b * n_kv + j) * T + t) * D) + 2 * c;
-            uint4* dst = reinterpret_cast<uint4*>(v_cache + ((size_t)(b * n_kv + j) * S + pos) * D) + 2 * c;
-            uint4 x0 = src[0], x1 = src[1];
-            dst[0] = x0;
-            dst[1] = x1;
-            continue;
-        }
-        const uint16_t* src;
-        uint16_t* dst;
-        if (head < n_q) {
-            src = q + ((size_t)(b * n_q + head) * T + t) * D;
-            dst = q_rot + ((size_t)(b * n_q + head) * T + t) * D;
-        } else {
-            const int j = head - n_q;
-            src = k_new + ((size_t)(b * n_kv + j) * T + t) * D;
-            dst = k_cache + ((size_t)(b * n_kv + j) * S + pos) * D;
-        }
-        // two 16-byte pieces holding 8 (a, b) pairs
-        const int off0 = rp.layout == 0 ? 16 * c : 8 * c;
-        const int off1 = rp.layout == 0 ? 16 * c + 8 : HALF + 8 * c;
-        uint4 x0 = *reinterpret_cast<const uint4*>(src + off0);
-        uint4 x1 = *reinterpret_cast<const uint4*>(src + off1);
-        uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        uint32_t o[8];
-        if (rp.layout == 0) {
-            // interleaved: word m holds pair 8c + m as (lo, hi) = (a, b)
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int i = 8 * c + m;
-                uint32_t ra, rb;
-                turn(bf_lo(w[m]), bf_hi(w[m]), s_cos[i], s_sin[i], ra, rb);
-                o[m] = ra | (rb << 16);
-            }
-        } else {
-            // half: value m of piece 0 pairs with value m of piece 1 (pair 8c + m)
-#pragma unroll
-            for (int m = 0; m < 8; m += 2) {
-                const int i = 8 * c + m;
-                uint32_t ra0, rb0, ra1, rb1;
-                turn(bf_lo(w[m / 2]), bf_lo(w[4 + m / 2]), s_cos[i], s_sin[i], ra0, rb0);
-                turn(bf_hi(w[m / 2]), bf_hi(w[4 + m / 2]), s_cos[i + 1], s_sin[i + 1], ra1, rb1);
-                o[m / 2] = ra0 | (ra1 << 16);
-                o[4 + m / 2] = rb0 | (rb1 << 16);
-            }
-        }
-        *reinterpret_cast<uint4*>(dst + off0) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4*>(dst + off1) = make_uint4(o[4], o[5], o[6], o[7]);
+    uint16_t* dst;
+    if (is_v) {
+        dst = v_cache + ((size_t)(b * n_kv + head - n_q - n_kv) * S + pos) * D;
+        *reinterpret_cast<uint4*>(dst + off0) = x0;
+        *reinterpret_cast<uint4*>(dst + off1) = x1;
+        return;
     }
+    dst = is_k ? k_cache + ((size_t)(b * n_kv + head - n_q) * S + pos) * D
+               : q_rot + ((size_t)(b * n_q + head) * T + t) * D;
+    uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t o[8];
+    if (rp.layout == 0) {
+        // interleaved: word m holds pair 8c + m as (lo, hi) = (a, b)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int i = 8 * c + m;
+            uint32_t ra, rb;
+            turn(bf_lo(w[m]), bf_hi(w[m]), s_cos[i], s_sin[i], ra, rb);
+            o[m] = ra | (rb << 16);
+        }
+    } else {
+        // half: value m of piece 0 pairs with value m of piece 1 (pair 8c + m)
+#pragma unroll
+        for (int m = 0; m < 8; m += 2) {
+            const int i = 8 * c + m;
+            uint32_t ra0, rb0, ra1, rb1;
+            turn(bf_lo(w[m / 2]), bf_lo(w[4 + m / 2]), s_cos[i], s_sin[i], ra0, rb0);
+            turn(bf_hi(w[m / 2]), bf_hi(w[4 + m / 2]), s_cos[i + 1], s_sin[i + 1], ra1, rb1);
+            o[m / 2] = ra0 | (ra1 << 16);
+            o[4 + m / 2] = rb0 | (rb1 << 16);
+        }
+    }
+    *reinterpret_cast<uint4*>(dst + off0) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + off1) = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 }  // namespace
@@ -143,7 +152,8 @@ hipError_t launch_rope_append(const uint16_t* q, uint16_t* q_rot, const uint16_t
     // grid.y is limited to 65535 sequences per launch: slice larger batches
     for (int b0 = 0; b0 < B; b0 += 65535) {
         const int nb = (B - b0) < 65535 ? (B - b0) : 65535;
-        dim3 grid(T, nb);
+        const int items = (n_q + 2 * n_kv) * (d / 16);
+        dim3 grid(T, nb, (items + 255) / 256);
         const size_t qo = (size_t)b0 * n_q * T * d, ko = (size_t)b0 * n_kv * T * d, co = (size_t)b0 * n_kv * S * d;
         prof_begin(K_ROPE_APPEND, st);
         if (d == 128)

@@ -103,6 +103,12 @@ int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v
  * gqa_decode_workspace_bytes -- bytes of device workspace gqa_decode_attn
  * needs for this shape (0 when the shape is invalid).  The size depends only
  * on the arguments and on library constants, not on past_len.
+ *
+ * The first 256 bytes of a workspace are a scheduling header (the counter
+ * that hands out work chunks).  They must be zero before the first
+ * gqa_decode_attn call that uses the workspace (allocate it zero-filled, or
+ * clear it once); every call leaves them zero again when it completes.  Calls
+ * that use one workspace must not overlap in time (order them on one stream).
  */
 size_t gqa_decode_workspace_bytes(int B, int n_q, int n_kv, int d, int S);
 
@@ -117,15 +123,20 @@ size_t gqa_decode_workspace_bytes(int B, int n_q, int n_kv, int d, int S);
  * itself is concatenation").  Each KV head's rows are read from memory once
  * for all g query heads of its group.
  *
- * The work is split over the rows ("split-K"); each split writes
- * (max, sum, partial output) records into the workspace, and a second kernel
- * merges them in a fixed order, so results are bitwise reproducible.
+ * The work is split over the rows ("split-K"): most of it in equal
+ * contiguous shares per workgroup, the rest in small fixed chunks taken from
+ * a counter in the workspace header as workgroups become free.  Each part
+ * writes (max, sum, partial output) records into the workspace, and a second
+ * kernel merges them in a fixed order.  Which rows form a part does not
+ * depend on timing, so results are bitwise reproducible for a given launch
+ * shape.
  *
  *   q_rot     in  [B, n_q, 1, d] bf16 (already rotated)
  *   k_cache   in  [B, n_kv, S, d] bf16;  v_cache likewise
  *   past_len  in  [B] int32 (device); rows 0..past_len[b] are attended
  *   out       out [B, n_q, 1, d] bf16
- *   workspace device scratch of at least gqa_decode_workspace_bytes(...)
+ *   workspace device scratch of at least gqa_decode_workspace_bytes(...),
+ *             header zeroed before its first use (see above)
  *   scale     score scale; <= 0 selects 1/sqrt(d)
  * Errors: INVALID_ARG, GROUP, HEAD_DIM, RANGE (max_past_len + 1 > S),
  *         WORKSPACE, HIP.
@@ -176,6 +187,15 @@ int gqa_profile_reset(void);
  * floating-point rounding.  Returns the value in effect.
  */
 int gqa_set_decode_workgroups(int n);
+
+/*
+ * Work-schedule override for tests and tuning: static_permille (0..1000) of
+ * the decode tiles are split into equal static shares, the rest into chunks of
+ * chunk_tiles (>= 1) tiles handed out dynamically.  (-1, 0) restores the
+ * defaults.  Results do not depend on it beyond floating-point rounding.
+ * Returns GQA_OK or GQA_ERR_INVALID_ARG.
+ */
+int gqa_set_decode_schedule(int static_permille, int chunk_tiles);
 
 #ifdef __cplusplus
 }

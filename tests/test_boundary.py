@@ -139,3 +139,13 @@ def test_decode_workgroup_override_clamps():
     assert gq.gqa_set_decode_workgroups(-3) == 0
     assert gq.gqa_set_decode_workgroups(10 ** 6) > 0
     assert gq.gqa_set_decode_workgroups(0) == 0
+
+
+def test_decode_schedule_override_validates():
+    assert gq.gqa_set_decode_schedule(700, 2) is None
+    assert gq.gqa_set_decode_schedule(0, 1) is None
+    assert gq.gqa_set_decode_schedule(1000, 64) is None
+    for bad in ((1001, 2), (-5, 2), (500, 0), (500, -1)):
+        with pytest.raises(ValueError):
+            gq.gqa_set_decode_schedule(*bad)
+    gq.gqa_set_decode_schedule()  # defaults

@@ -130,19 +130,21 @@ DECODE_CASES = [
 ]
 
 
-def run_decode_e2e(case, seed, wg=0):
+def run_decode_e2e(case, seed, wg=0, schedule=(-1, 0)):
     B, n_q, n_kv, d, S, past, theta, layout, scaling = case
     q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed)
     q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
     ref = attend(q_ref, kc_ref, vc_ref, past, n_kv)
     kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
     gq.gqa_set_decode_workgroups(wg)
+    gq.gqa_set_decode_schedule(*schedule)
     try:
         q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling)
         out = gq.gqa_decode_attn(q_rot, kc_d, vc_d, pl, max(past))
         torch.cuda.synchronize()
     finally:
         gq.gqa_set_decode_workgroups(0)
+        gq.gqa_set_decode_schedule()
     return synth.bits(out), ref, (q_rot, kc_d, vc_d, pl)
 
 
@@ -180,6 +182,37 @@ def test_decode_workgroup_count_invariance_and_determinism():
         outs.append(got)
     again, _, _ = run_decode_e2e(case, seed=77, wg=0)
     assert np.array_equal(again, outs[-1]), "same launch shape must give bitwise identical results"
+
+
+@pytest.mark.parametrize("wg", [0, 37])
+def test_decode_schedule_invariance_and_determinism(wg):
+    """All-static, all-dynamic and mixed work splits, chunk sizes 1..5: same results to the tolerance, and a
+    repeated call with the same launch shape and schedule is bitwise identical."""
+    case = (6, 32, 8, 128, 3000, [2999, 0, 700, 1500, 64, 2100], 5.0e5, "interleaved", None)
+    say(f"decode schedule sweep wg={wg}")
+    for sched in ((1000, 2), (0, 1), (0, 2), (500, 3), (700, 2), (300, 5)):
+        got, ref, _ = run_decode_e2e(case, seed=91, wg=wg, schedule=sched)
+        check_out(got, ref, f"decode wg={wg} schedule={sched}")
+        again, _, _ = run_decode_e2e(case, seed=91, wg=wg, schedule=sched)
+        assert np.array_equal(again, got), f"schedule {sched}: repeated call differs"
+
+
+def test_decode_workspace_reuse_leaves_header_zero():
+    """One caller-owned workspace serves consecutive calls of different sizes; each call clears the
+    scheduling header it used."""
+    say("decode workspace reuse")
+    B, n_q, n_kv, d, S = 4, 32, 8, 128, 2500
+    ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    for it, past in enumerate(([2400, 10, 999, 1800], [5, 2499, 64, 300], [1, 1, 1, 1])):
+        q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=500 + it)
+        for b in range(B):  # row past_len is attended here: make it finite
+            kc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 600 + 10 * it + b))
+            vc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 700 + 10 * it + b))
+        ref = attend(q, kc, vc, past, n_kv)
+        out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), workspace=ws)
+        torch.cuda.synchronize()
+        check_out(synth.bits(out), ref, f"decode reuse call {it}")
+        assert int(ws[:256].count_nonzero()) == 0, "scheduling header must be zero after a call"
 
 
 def test_decode_scale_argument():
