@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// the same with the gfx950 conversion instruction (v_cvt_pk_bf16_f32, round to
+// nearest even): one instruction for two values
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 // fp64 -> bf16 rounded once to nearest even.  The value is first narrowed to
 // fp32 with round-to-odd (truncate toward zero, then set the last bit when
 // anything was dropped); fp32 keeps 16 more bits than bf16, so rounding that

@@ -98,33 +98,36 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
     const uint16_t* kbase = k_cache + (size_t)(b * n_kv + j) * S * D;
     const uint16_t* vbase = v_cache + (size_t)(b * n_kv + j) * S * D;
 
-    uint4 kst[K_LOADS];
-    uint4 vst[V_ITEMS][2];
+    // Raw buffer loads over the visible rows only: the descriptor range is
+    // kv_end rows, so the hardware returns zeros for keys past the last row any
+    // query of this workgroup can see (no per-row branch, no read beyond them).
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kv_end * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, kv_end * D * 2, 0x00020000);
+    u32x4_t kst[K_LOADS];
+    u32x4_t vst[V_ITEMS][2];
     auto load = [&](int tile) {
-        const int key0 = tile * KT;
+        const int soff = tile * KT * D * 2;
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) {
             const int pi = tid + NTHR * i;
             const int key = pi / PPR, c = pi % PPR;
-            kst[i] = key0 + key < kv_end ? *reinterpret_cast<const uint4*>(kbase + (size_t)(key0 + key) * D + 8 * c)
-                                         : make_uint4(0, 0, 0, 0);
+            kst[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (key * D + 8 * c) * 2, soff, 0);
         }
 #pragma unroll
         for (int i = 0; i < V_ITEMS; ++i) {
             const int it = tid + NTHR * i;
             const int kp = it % (KT / 2), c = it / (KT / 2);
-            const int k0 = key0 + 2 * kp;
-            vst[i][0] = k0 < kv_end ? *reinterpret_cast<const uint4*>(vbase + (size_t)k0 * D + 8 * c)
-                                    : make_uint4(0, 0, 0, 0);
-            vst[i][1] = k0 + 1 < kv_end ? *reinterpret_cast<const uint4*>(vbase + (size_t)(k0 + 1) * D + 8 * c)
-                                        : make_uint4(0, 0, 0, 0);
+            vst[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rv, (2 * kp * D + 8 * c) * 2, soff, 0);
+            vst[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * kp + 1) * D + 8 * c) * 2, soff, 0);
         }
     };
     auto store = [&]() {
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) {
             const int pi = tid + NTHR * i;
-            s_k[kpos<PPR>(pi / PPR, pi % PPR)] = kst[i];
+            s_k[kpos<PPR>(pi / PPR, pi % PPR)] = __builtin_bit_cast(uint4, kst[i]);
         }
 #pragma unroll
         for (int i = 0; i < V_ITEMS; ++i) {
@@ -174,29 +177,37 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
             }
         }
 
-        // ---- scale, mask, online softmax per query row
+        // ---- mask (only tiles that cross a row's causal bound), online softmax per query row
         const int key0 = tile * KT;
-        const bool masked_tile = tile >= first_masked_tile;
-        // [hi/lo][kb][nb][word]: the weights as PV B operands, split p = hi + lo with both parts
+        if (tile >= first_masked_tile) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int lim = P + row_t[nb];  // last visible key of this row
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (key0 + 16 * mb + 4 * lq + i > lim) sacc[mb][nb][i] = -INFINITY;
+            }
+        }
+        // [hi/lo][kb][nb]: the weights as PV B operands, split p = hi + lo with both parts
         // in bf16 so the product with V keeps ~16 significant bits of p
-        uint32_t pk[2][2][2][4];
+        u32x4_t pk[2][2][2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            const int lim = P + row_t[nb];  // last visible key of this row
             float mx = -INFINITY;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float s = sacc[mb][nb][i] * scale_log2;
-                    if (masked_tile && key0 + 16 * mb + 4 * lq + i > lim) s = -INFINITY;
-                    sacc[mb][nb][i] = s;
-                    mx = fmaxf(mx, s);
-                }
+            for (int mb = 0; mb < 4; ++mb) mx = fmaxf(mx, fmaxf(fmaxf(sacc[mb][nb][0], sacc[mb][nb][1]),
+                                                              fmaxf(sacc[mb][nb][2], sacc[mb][nb][3])));
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m_run[nb], mx);  // finite: key 0 is visible to every row
-            const float alpha = fast_exp2(m_run[nb] - mn);
+            // The exponent reference m_ref (scaled, base 2) only moves when the row
+            // maximum exceeds it by more than 8: weights then stay below 2^8, and
+            // the accumulators are rescaled rarely instead of on every tile.
+            const float mxs = mx * scale_log2;  // finite: key 0 is visible to every row
+            const bool move = mxs > m_run[nb] + 8.f;
+            const float mn = move ? mxs : m_run[nb];
+            const float alpha = move ? fast_exp2(m_run[nb] - mn) : 1.f;
             m_run[nb] = mn;
             float ps = 0.f;
 #pragma unroll
@@ -204,23 +215,23 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(sacc[mb][nb][i] - mn);
+                    p[i] = fast_exp2(__builtin_fmaf(sacc[mb][nb][i], scale_log2, -mn));
                     ps += p[i];
                 }
-                uint32_t hb[4], lb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    hb[i] = f32_to_bf16_rne(p[i]);
-                    lb[i] = f32_to_bf16_rne(p[i] - __uint_as_float(hb[i] << 16));
-                }
-                pk[0][mb >> 1][nb][(mb & 1) * 2 + 0] = hb[0] | (hb[1] << 16);
-                pk[0][mb >> 1][nb][(mb & 1) * 2 + 1] = hb[2] | (hb[3] << 16);
-                pk[1][mb >> 1][nb][(mb & 1) * 2 + 0] = lb[0] | (lb[1] << 16);
-                pk[1][mb >> 1][nb][(mb & 1) * 2 + 1] = lb[2] | (lb[3] << 16);
+                const uint32_t h01 = cvt_pk_bf16(p[0], p[1]), h23 = cvt_pk_bf16(p[2], p[3]);
+                const uint32_t l01 = cvt_pk_bf16(p[0] - bf_lo(h01), p[1] - bf_hi(h01));
+                const uint32_t l23 = cvt_pk_bf16(p[2] - bf_lo(h23), p[3] - bf_hi(h23));
+                const int w0 = (mb & 1) * 2;
+                pk[0][mb >> 1][nb][w0] = h01;
+                pk[0][mb >> 1][nb][w0 + 1] = h23;
+                pk[1][mb >> 1][nb][w0] = l01;
+                pk[1][mb >> 1][nb][w0 + 1] = l23;
             }
             l_run[nb] = l_run[nb] * alpha + ps;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db][nb] *= alpha;
+                for (int db = 0; db < DB; ++db) oacc[db][nb] *= alpha;
+            }
         }
 
         // ---- O^T += V^T P^T
@@ -230,9 +241,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    bop[hl][nb] = __builtin_bit_cast(
-                        bf16x8_t, make_uint4(pk[hl][kb][nb][0], pk[hl][kb][nb][1], pk[hl][kb][nb][2], pk[hl][kb][nb][3]));
+                for (int nb = 0; nb < 2; ++nb) bop[hl][nb] = __builtin_bit_cast(bf16x8_t, pk[hl][kb][nb]);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int dim = 16 * db + l16;
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         for (int db = 0; db < DB; ++db) {
             const f32x4_t o = oacc[db][nb];
             *reinterpret_cast<uint2*>(dst + 16 * db + 4 * lq) =
-                make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+                make_uint2(cvt_pk_bf16(o[0] * inv, o[1] * inv), cvt_pk_bf16(o[2] * inv, o[3] * inv));
         }
     }
 }
