@@ -66,11 +66,11 @@ constexpr int OOB = 0x7ffffff0;               // a buffer offset past any range:
 
 template <int D, int HGW, int NHG>
 struct Cfg {
-    static constexpr int NP = D / 64;              // 16-byte pieces per lane per row
     static constexpr int PPR = D / 8;              // 16-byte pieces per row
     static constexpr int RG = WAVES / NHG;         // row groups per tile
     static constexpr int ROWS_W = TILE / RG;       // rows of a tile one wave handles
-    static constexpr int PASSES = ROWS_W / 8;      // q.k passes of 8 rows
+    static constexpr int KB = ROWS_W / 16;         // 16-row blocks of a wave (one MFMA output block each)
+    static constexpr int KS = D / 32;              // MFMA k-steps over the head dimension
     static constexpr int GC = HGW * NHG;           // heads per segment
     static constexpr int REC = D + 4;              // m, l, 2 pad, o[D]
     static constexpr int SLOT = GC * REC;          // floats per piece (one merged record per head)
@@ -134,6 +134,14 @@ template <int D>
 __device__ __forceinline__ int lds_byte(int R, int c) {
     return D == 128 ? R * 256 + ((c ^ (((R >> 1) & 1) << 3)) << 4) : R * 128 + (c << 4);
 }
+// Byte offset of piece c of row R in the LDS K tile, read as MFMA A operands:
+// 16 lanes read one piece index of 16 consecutive rows, so the piece slot is
+// XOR-ed with the row's low bits and those 16 reads hit distinct banks.
+template <int D>
+__device__ __forceinline__ int kpos_byte(int R, int c) {
+    constexpr int PPR = D / 8;
+    return R * (D * 2) + ((c ^ (R & (PPR - 1))) << 4);
+}
 
 // Tile schedule shared by the partial and combine kernels: tiles [0, Ts) are
 // split into equal contiguous shares, tiles [Ts, T_all) into chunks of C.
@@ -166,13 +174,13 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const int32_t* __restrict__ past_len, int pmax, float* __restrict__ ws, int B, int n_q, int n_kv, int S, int nhc,
     float scale_log2, int static_pm, int chunk) {
     using C = Cfg<D, HGW, NHG>;
-    constexpr int NP = C::NP, PASSES = C::PASSES;
+    constexpr int KB = C::KB, KS = C::KS;
     constexpr int DPL = D / 64;                  // value dims each lane accumulates
     constexpr int ROWB = D * 2;                  // bytes per cache row
     constexpr int TILEB = TILE * ROWB;           // bytes per K (or V) tile
     constexpr int HALF = C::LOADS / 2;           // 16-byte loads per thread per K (or V) tile
     __shared__ __align__(16) unsigned char s_kv[2 * TILEB];  // K tile, then V tile
-    __shared__ float4 s_p[THREADS / 64][PASSES][8];          // softmax weights of each wave's rows
+    __shared__ float4 s_p[THREADS / 64][C::ROWS_W];         // softmax weights of each wave's rows (4 heads)
     __shared__ u32x4_t s_q[C::GC * (D / 8)];                  // the segment's GC query rows
     __shared__ int s_wsum[THREADS / 64];
     // state of each wave when a piece ends: o[D], m at D, l at D+1
@@ -194,7 +202,6 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int r = lane >> 3, e = lane & 7;
     const int hg = wave / C::RG, rg = wave % C::RG;
     const int rbase = rg * C::ROWS_W;
     const int g = n_q / n_kv;
@@ -313,19 +320,33 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     };
 
     // LDS position of the bytes this thread loaded: row tid*16/ROWB + i*(4096/ROWB), piece (tid*16 % ROWB)/16;
-    // the swizzle bit depends only on tid, so every store is base + constant.
-    const int st_base = lds_byte<D>((tid * 16) / ROWB, ((tid * 16) % ROWB) >> 4);
+    // both swizzles depend only on tid, so every store is base + constant.
+    const int st_base = lds_byte<D>((tid * 16) / ROWB, ((tid * 16) % ROWB) >> 4);  // V tile
+    const int stk_base = kpos_byte<D>((tid * 16) / ROWB, ((tid * 16) % ROWB) >> 4);  // K tile
 
-    // ---- per-wave softmax state for its HGW heads; lane owns value dims DPL*lane ..
-    float m_run[HGW], l_run[HGW];
+    // ---- per-wave softmax state.  Scores live in the MFMA output layout: lane
+    // (n = lane % 16, lq = lane / 16) holds head n (n < HGW) at 4 of the rows of
+    // each 16-row block, so m_run (the head's running max, equal in its four
+    // lanes) and l_run (this lane's share of the head's running sum) belong to
+    // head n.  For the weighted value sum every lane owns DPL value dims of all
+    // of the wave's heads.
+    const int l16 = lane & 15, lq = lane >> 4;
+    float m_run, l_run;
     float o[HGW][DPL];
+    bf16x8_t qop[KS];  // B operand: 8 dims of head l16 per k-step (zero for l16 >= HGW)
     auto reset_state = [&] __attribute__((always_inline)) () {
+        m_run = -INFINITY;
+        l_run = 0.f;
 #pragma unroll
-        for (int h = 0; h < HGW; ++h) {
-            m_run[h] = -INFINITY;
-            l_run[h] = 0.f;
+        for (int h = 0; h < HGW; ++h)
 #pragma unroll
             for (int x = 0; x < DPL; ++x) o[h][x] = 0.f;
+    };
+    auto load_qop = [&] __attribute__((always_inline)) () {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4_t v = s_q[(hg * HGW + (l16 < HGW ? l16 : 0)) * (D / 8) + 4 * ks + lq];
+            qop[ks] = __builtin_bit_cast(bf16x8_t, l16 < HGW ? v : u32x4_t{0u, 0u, 0u, 0u});
         }
     };
     auto park = [&] __attribute__((always_inline)) () {
@@ -336,9 +357,11 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
                 *reinterpret_cast<float2*>(pk + 2 * lane) = make_float2(o[h][0], o[h][DPL - 1]);
             else
                 pk[lane] = o[h][0];
-            const float l = sum_hi3(l_run[h]);
-            if (lane == 0) *reinterpret_cast<float2*>(pk + D) = make_float2(m_run[h], l);
         }
+        float l = l_run;
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (lane < HGW) *reinterpret_cast<float2*>(&s_park[wave][lane][D]) = make_float2(m_run, l);
     };
     // Merge the parked wave states of the finished piece into one record per
     // head and store it.  The stores are issued on every call; with
@@ -396,110 +419,96 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         }
     };
 
-    // LDS read bases.  q.k: lane (r, e) reads pieces e + 8pp of rows rbase + 2r + const.
-    int qk_base[NP];
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) qk_base[pp] = lds_byte<D>(rbase + 2 * r, e + 8 * pp);
     // value sum: every lane reads its DPL dims of a row; the swizzle depends on the row's parity class.
     const int pv_base0 = D == 128 ? lds_byte<D>(rbase, lane >> 2) + (lane & 3) * 4 : rbase * ROWB + lane * 2;
     const int pv_base1 = D == 128 ? lds_byte<D>(rbase + 2, lane >> 2) + (lane & 3) * 4 - 2 * ROWB : pv_base0;
 
-    // ---- one tile: q.k, online softmax, weighted value sum (this wave's rows and heads)
-    auto compute_tile = [&] __attribute__((always_inline)) (int c_tt, int c_L) {
-        const int row0 = c_tt * TILE;
-        float sc[PASSES][HGW];
+    // ---- one tile: q.k on MFMA, online softmax, weighted value sum (this wave's rows and heads)
+    // vrows: rows of the tile inside the segment's valid range (1..64)
+    auto compute_tile = [&] __attribute__((always_inline)) (int vrows) {
+        // S^T = K Q^T: A = 16 K rows x 32 dims (lane: row l16, dims 8 lq + 0..7), B = Q^T
+        f32x4_t sacc[KB];
 #pragma unroll
-        for (int k = 0; k < PASSES; ++k) {
-            const int dR = 16 * (k >> 1) + (k & 1);  // row offset of this pass (rows rbase + 2r + dR)
-            u32x4_t kp[NP];
+        for (int kb = 0; kb < KB; ++kb) {
+            sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp)
-                kp[pp] = *reinterpret_cast<const u32x4_t*>(s_kv + qk_base[pp] + dR * ROWB);
-            u32x4_t qv[HGW][NP];
-#pragma unroll
-            for (int h = 0; h < HGW; ++h)
-#pragma unroll
-                for (int pp = 0; pp < NP; ++pp) qv[h][pp] = s_q[(hg * HGW + h) * (D / 8) + e + 8 * pp];
-            const bool valid = row0 + rbase + 2 * r + dR < c_L;
-#pragma unroll
-            for (int h = 0; h < HGW; ++h) {
-                float acc = 0.f;
-#pragma unroll
-                for (int pp = 0; pp < NP; ++pp) {
-                    acc = dot2_bf16(kp[pp].x, qv[h][pp].x, acc);
-                    acc = dot2_bf16(kp[pp].y, qv[h][pp].y, acc);
-                    acc = dot2_bf16(kp[pp].z, qv[h][pp].z, acc);
-                    acc = dot2_bf16(kp[pp].w, qv[h][pp].w, acc);
-                }
-                acc = sum8(acc);
-                sc[k][h] = valid ? acc * scale_log2 : -INFINITY;
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4_t kv =
+                    *reinterpret_cast<const u32x4_t*>(s_kv + kpos_byte<D>(rbase + 16 * kb + l16, 4 * ks + lq));
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qop[ks],
+                                                                     sacc[kb], 0, 0, 0);
             }
         }
-        // online softmax (base-2 exponent: scores already carry the log2 e factor)
-        float alpha[HGW];
+        // online softmax for head l16 over rows rbase + 16 kb + 4 lq + i (base-2 exponent)
+        float sc[KB][4];
+        float tm = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = rbase + 16 * kb + 4 * lq + i < vrows;
+                sc[kb][i] = valid ? sacc[kb][i] * scale_log2 : -INFINITY;
+                tm = fmaxf(tm, sc[kb][i]);
+            }
+        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        const float mn = fmaxf(m_run, tm);
+        const float mref = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m_run - mn);
+        m_run = mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[kb][i] = fast_exp2(sc[kb][i] - mref);
+                ps += sc[kb][i];
+            }
+        l_run = l_run * alpha + ps;
+        // weights to LDS: s_p[wave][row][head]
+        if (l16 < HGW) {
+            float* sp = reinterpret_cast<float*>(s_p[wave]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sp[(16 * kb + 4 * lq + i) * 4 + l16] = sc[kb][i];
+        }
 #pragma unroll
         for (int h = 0; h < HGW; ++h) {
-            float tm = sc[0][h];
+            const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
 #pragma unroll
-            for (int k = 1; k < PASSES; ++k) tm = fmaxf(tm, sc[k][h]);
-            tm = max_hi3(tm);
-            const float mn = fmaxf(m_run[h], tm);
-            const float mref = (mn == -INFINITY) ? 0.f : mn;
-            alpha[h] = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[h] - mn);
-            m_run[h] = mn;
-            float ps = 0.f;
-#pragma unroll
-            for (int k = 0; k < PASSES; ++k) {
-                sc[k][h] = fast_exp2(sc[k][h] - mref);
-                ps += sc[k][h];
-            }
-            l_run[h] = l_run[h] * alpha[h] + ps;
-#pragma unroll
-            for (int x = 0; x < DPL; ++x) o[h][x] *= alpha[h];
-        }
-        // weights to LDS (one lane per row), then every lane sums its value dims over the rows
-        if (e == 0) {
-#pragma unroll
-            for (int k = 0; k < PASSES; ++k) {
-                float pv[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int h = 0; h < HGW; ++h) pv[h] = sc[k][h];
-                s_p[wave][k][r] = make_float4(pv[0], pv[1], pv[2], pv[3]);
-            }
+            for (int x = 0; x < DPL; ++x) o[h][x] *= ah;
         }
         __builtin_amdgcn_wave_barrier();
         const unsigned char* vt = s_kv + TILEB;
 #pragma unroll
-        for (int k = 0; k < PASSES; ++k) {
+        for (int rr = 0; rr < C::ROWS_W; ++rr) {
+            const float4 p4 = s_p[wave][rr];
+            const float pw[4] = {p4.x, p4.y, p4.z, p4.w};
+            if (DPL == 2) {
+                // row rbase + rr (rbase is a multiple of 16): its swizzle class is (rr >> 1) & 1
+                const uint32_t vw =
+                    *reinterpret_cast<const uint32_t*>(vt + (((rr >> 1) & 1) ? pv_base1 : pv_base0) + rr * ROWB);
+                const float v0 = bf_lo(vw), v1 = bf_hi(vw);
 #pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                const int dR = 16 * (k >> 1) + 2 * rr + (k & 1);  // row rbase + dR; parity class of dR>>1 is rr&1
-                const float4 p4 = s_p[wave][k][rr];
-                const float pw[4] = {p4.x, p4.y, p4.z, p4.w};
-                if (DPL == 2) {
-                    const uint32_t vw =
-                        *reinterpret_cast<const uint32_t*>(vt + ((rr & 1) ? pv_base1 : pv_base0) + dR * ROWB);
-                    const float v0 = bf_lo(vw), v1 = bf_hi(vw);
-#pragma unroll
-                    for (int h = 0; h < HGW; ++h) {
-                        o[h][0] += pw[h] * v0;
-                        o[h][DPL - 1] += pw[h] * v1;
-                    }
-                } else {
-                    const uint32_t vh = *reinterpret_cast<const uint16_t*>(vt + pv_base0 + dR * ROWB);
-                    const float v0 = __uint_as_float(vh << 16);
-#pragma unroll
-                    for (int h = 0; h < HGW; ++h) o[h][0] += pw[h] * v0;
+                for (int h = 0; h < HGW; ++h) {
+                    o[h][0] += pw[h] * v0;
+                    o[h][DPL - 1] += pw[h] * v1;
                 }
-                // keep at most two rows' LDS reads in flight: the empty asm pins the
-                // accumulators here, so the sums above cannot sink below later reads
-                if (rr & 1) {
+            } else {
+                const uint32_t vh = *reinterpret_cast<const uint16_t*>(vt + pv_base0 + rr * ROWB);
+                const float v0 = __uint_as_float(vh << 16);
 #pragma unroll
-                    for (int h = 0; h < HGW; ++h)
+                for (int h = 0; h < HGW; ++h) o[h][0] += pw[h] * v0;
+            }
+            // keep at most two rows' LDS reads in flight: the empty asm pins the
+            // accumulators here, so the sums above cannot sink below later reads
+            if (rr & 1) {
 #pragma unroll
-                        for (int x = 0; x < DPL; ++x) asm volatile("" : "+v"(o[h][x]));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (int h = 0; h < HGW; ++h)
+#pragma unroll
+                    for (int x = 0; x < DPL; ++x) asm volatile("" : "+v"(o[h][x]));
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         pend = false;
 #pragma unroll
         for (int x = 0; x < HALF; ++x) {
-            *reinterpret_cast<u32x4_t*>(s_kv + st_base + x * THREADS * 16) = buf[x];
+            *reinterpret_cast<u32x4_t*>(s_kv + stk_base + x * THREADS * 16) = buf[x];
             *reinterpret_cast<u32x4_t*>(s_kv + TILEB + st_base + x * THREADS * 16) = buf[HALF + x];
         }
         if (seg_start && tid < QPIECES) s_q[tid] = qbuf;
@@ -539,9 +548,10 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
             take_ticket(uni(s_ticket));
             pending = false;
         }
+        if (seg_start) load_qop();
         issue(buf, qbuf, tkbuf, stg);
         if ((cs.flags & KIND_MASK) == K_TILE) {
-            compute_tile(cs.tt, cs.L);
+            compute_tile(cs.L - cs.tt * TILE);
             seg_start = (cs.flags & F_PIECE_END) != 0;
             if (seg_start) {
                 park();
@@ -567,22 +577,27 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
 
 // Merge of the partial records of one (sequence, query head), in a fixed
 // order: the static shares that hold tiles of the head's segment, in
-// workgroup order, then its chunks in chunk order.  Records are taken in
-// batches of 16 whose loads are all in flight together, and merged online
-// (running max, rescaled sum and output).  Block (0, 0) also clears the ticket
-// counter, so the next call starts from zero.
+// workgroup order, then its chunks in chunk order.  Four waves share the
+// records (wave k takes records k, k+4, ...), each merging its own online
+// (running max, rescaled sum and output) with all of its loads in flight
+// together; the four states then merge in wave order through LDS.  Block
+// (0, 0) also clears the ticket counter, so the next call starts from zero.
+constexpr int CMB_WAVES = 4;
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ ws,
-                                                            const int32_t* __restrict__ past_len, int pmax,
-                                                            uint16_t* __restrict__ out, int B, int n_q, int n_kv,
-                                                            int nhc, int gc, int G, int static_pm, int chunk) {
+__global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* __restrict__ ws,
+                                                                        const int32_t* __restrict__ past_len,
+                                                                        int pmax, uint16_t* __restrict__ out, int B,
+                                                                        int n_q, int n_kv, int nhc, int gc, int G,
+                                                                        int static_pm, int chunk) {
     constexpr int DPL = D / 64;  // dims per lane
     constexpr int REC = D + 4;
-    constexpr int RB = 16;       // records per batch
+    constexpr int RB = 8;        // records per wave and batch
+    __shared__ float s_acc[CMB_WAVES][D];
+    __shared__ float2 s_ml[CMB_WAVES];
     const int h = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = n_q / n_kv;
-    if (h == 0 && b == 0 && lane == 0) reinterpret_cast<int*>(ws)[0] = 0;
+    if (h == 0 && b == 0 && tid == 0) reinterpret_cast<int*>(ws)[0] = 0;
     const float* recs = ws + HDR_FLOATS;
     const size_t slot_floats = (size_t)gc * REC;
 
@@ -643,13 +658,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ 
     float M = -INFINITY, L = 0.f, acc[DPL];
 #pragma unroll
     for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-    for (int base = 0; base < nrec; base += RB) {
+    for (int base = wave; base < nrec; base += CMB_WAVES * RB) {
         float2 ml[RB];
         float ov[RB][DPL];
         bool use[RB];
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
-            const float* rp = recs + (size_t)slot_of(base + u, use[u]) * slot_floats + (size_t)hl * REC;
+            const float* rp =
+                recs + (size_t)slot_of(base + CMB_WAVES * u, use[u]) * slot_floats + (size_t)hl * REC;
             ml[u] = *reinterpret_cast<const float2*>(rp);
 #pragma unroll
             for (int x = 0; x < DPL; ++x) ov[u][x] = rp[4 + DPL * lane + x];
@@ -667,13 +683,32 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(float* __restrict__ 
             M = mn;
         }
     }
-
-    const float inv = 1.f / L;
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) s_acc[wave][DPL * lane + x] = acc[x];
+    if (lane == 0) s_ml[wave] = make_float2(M, L);
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < CMB_WAVES; ++k) Mt = fmaxf(Mt, s_ml[k].x);
+    float Lt = 0.f, o[DPL];
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) o[x] = 0.f;
+#pragma unroll
+    for (int k = 0; k < CMB_WAVES; ++k) {
+        const float2 mlk = s_ml[k];
+        if (mlk.x == -INFINITY) continue;
+        const float f = fast_exp2(mlk.x - Mt);
+        Lt += f * mlk.y;
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) o[x] += f * s_acc[k][DPL * lane + x];
+    }
+    const float inv = 1.f / Lt;
     uint16_t* dst = out + (size_t)(b * n_q + h) * D + DPL * lane;
     if (DPL == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[DPL - 1] * inv);
+        *reinterpret_cast<uint32_t*>(dst) = cvt_pk_bf16(o[0] * inv, o[DPL - 1] * inv);
     } else {
-        dst[0] = (uint16_t)f32_to_bf16_rne(acc[0] * inv);
+        dst[0] = (uint16_t)f32_to_bf16_rne(o[0] * inv);
     }
 }
 
@@ -803,10 +838,10 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
 
         prof_begin(K_DECODE_COMBINE, st);
         if (d == 128)
-            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64), 0, st, ws, pl, max_past_len, o,
+            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl, max_past_len, o,
                                nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk);
         else
-            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64), 0, st, ws, pl, max_past_len, o,
+            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl, max_past_len, o,
                                nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk);
         prof_end(K_DECODE_COMBINE, st);
         e = hipGetLastError();
