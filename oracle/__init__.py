@@ -11,6 +11,7 @@ whose values no page fixes (the blend band of Llama-3 scaled RoPE) says
 """
 
 from .gqa_oracle import (  # noqa: F401
+    visible_rows,
     bf16_to_f64,
     f64_to_bf16,
     rope_frequencies,

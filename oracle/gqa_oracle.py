@@ -29,6 +29,15 @@ Parity status:
                               longest ones divided by the factor, continuity).
   rotate_pairs / rope_append  pinned (complex multiplication, p = 0 identity,
                               relative-offset invariance, index rule, sizes)
+  visible_rows (window, sinks) pinned by reduction to the full mask (window at
+                              least the context, sinks covering it), the
+                              one-row window (the output is that value row),
+                              constant keys (the mean of the kept rows), and a
+                              window equal to full attention over the sliced
+                              cache; the reading of the window and sink rules
+                              is the plainest one the course outline supports
+  attend sink_logits          pinned by -inf (no sink), constant keys (closed
+                              form of the extra denominator term)
   attend                      pinned (brute force with materialised repeat_kv
                               and the printed mask construction, torch SDPA on
                               CPU, closed forms, MHA/MQA special cases,
@@ -208,15 +217,35 @@ def rope_append(q, k_new, v_new, k_cache, v_cache, past_len, theta, layout="inte
 # ---------------------------------------------------------------------------
 
 
-def attend(q_rot, k_cache, v_cache, past_len, n_kv, scale=None):
+def visible_rows(pos, L, window=0, n_sink=0):
+    """Boolean mask over cache rows 0 .. L-1 seen by the query at position pos.
+
+    Causal rule ([ATL] Transformer.forward excerpt): rows 0 .. pos.  With a
+    sliding window of W > 0 rows ([P7] modules L7.5 and L7.7 name the window
+    and StreamingLLM sinks; reading taken: the query sees its own row and the
+    W - 1 rows before it), only rows r > pos - W stay visible, except the first
+    n_sink rows (the sinks), which every query keeps seeing.
+    """
+    r = np.arange(L)
+    vis = r <= pos
+    if window > 0:
+        vis &= (r > pos - window) | (r < n_sink)
+    return vis
+
+
+def attend(q_rot, k_cache, v_cache, past_len, n_kv, scale=None, window=0, n_sink=0, sink_logits=None):
     """Grouped-query attention of the new queries over the cache, in fp64.
 
     Head map ([REP] formula; [EP18] "Our six heads, three ways"): query head
     h reads KV head floor(h / g) with g = n_q / n_kv.
     Scores ([KV] "The cache itself is concatenation"): q . k / sqrt(d).
     Mask ([ATL] Transformer.forward excerpt): new row t of a sequence with
-    past_len P is at position P + t and sees cache rows 0 .. P + t.
+    past_len P is at position P + t and sees cache rows 0 .. P + t; with a
+    window and sinks, see ``visible_rows``.
     Softmax over the visible rows, then the weighted sum of the value rows.
+    A learned sink ([P7] L7.5 / L7.7 "learned sinks"; reading taken: one extra
+    logit per query head that joins the softmax normaliser and carries no
+    value) adds exp(sink_logits[h]) to the denominator.
     Rows at or beyond P + T are never read.
 
     Returns float64 [B, n_q, T, d].
@@ -238,16 +267,22 @@ def attend(q_rot, k_cache, v_cache, past_len, n_kv, scale=None):
             V = bf16_to_f64(v_cache[b, j, :L])
             Q = bf16_to_f64(q_rot[b, j * g:(j + 1) * g]).reshape(g * T, d)
             s = (Q @ K.T) * scale
-            visible = np.arange(L)[None, :] <= (P + t_of_row)[:, None]
+            visible = np.stack([visible_rows(P + t, L, window, n_sink) for t in t_of_row])
             s = np.where(visible, s, -np.inf)
-            s = s - s.max(axis=1, keepdims=True)
-            w = np.exp(s)
-            w = w / w.sum(axis=1, keepdims=True)
+            if sink_logits is None:
+                top = s.max(axis=1, keepdims=True)
+                w = np.exp(s - top)
+                w = w / w.sum(axis=1, keepdims=True)
+            else:
+                sk = np.repeat(np.asarray(sink_logits, dtype=np.float64)[j * g:(j + 1) * g], T)[:, None]
+                top = np.maximum(s.max(axis=1, keepdims=True), sk)
+                w = np.exp(s - top)
+                w = w / (w.sum(axis=1, keepdims=True) + np.exp(sk - top))
             out[b, j * g:(j + 1) * g] = (w @ V).reshape(g, T, d)
     return out
 
 
-def attend_bruteforce(q_rot, k_cache, v_cache, past_len, n_kv, scale=None):
+def attend_bruteforce(q_rot, k_cache, v_cache, past_len, n_kv, scale=None, window=0, n_sink=0, sink_logits=None):
     """Second formulation of ``attend`` for tiny shapes: explicit loops.
 
     It follows the pages' own construction literally: the KV heads are
@@ -272,6 +307,11 @@ def attend_bruteforce(q_rot, k_cache, v_cache, past_len, n_kv, scale=None):
         v_rep = [vb[h // g] for h in range(n_q)]
         new_block = [[(-math.inf if col > row else 0.0) for col in range(T)] for row in range(T)]
         mask = [[0.0] * P + new_block[row] for row in range(T)]
+        if window > 0:  # rows that fell out of the window, other than the sinks
+            for t in range(T):
+                for r in range(L):
+                    if r <= P + t - window and r >= n_sink:
+                        mask[t][r] = -math.inf
         for h in range(n_q):
             for t in range(T):
                 scores = []
@@ -281,8 +321,12 @@ def attend_bruteforce(q_rot, k_cache, v_cache, past_len, n_kv, scale=None):
                         dot += q[b, h, t, c] * k_rep[h][r, c]
                     scores.append(dot * scale + mask[t][r])
                 top = max(scores)
+                extra = 0.0
+                if sink_logits is not None:
+                    top = max(top, float(sink_logits[h]))
+                    extra = math.exp(float(sink_logits[h]) - top)
                 weights = [math.exp(x - top) for x in scores]
-                total = sum(weights)
+                total = sum(weights) + extra
                 for c in range(d):
                     acc = 0.0
                     for r in range(L):

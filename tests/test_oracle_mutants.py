@@ -29,10 +29,13 @@ MUTANTS = {
                            "freq = np.power(float(theta), -(1.0 * i) / d)"),
     "head map modulo": ("Q = bf16_to_f64(q_rot[b, j * g:(j + 1) * g]).reshape(g * T, d)",
                         "Q = bf16_to_f64(q_rot[b, j::n_kv]).reshape(g * T, d)"),
-    "mask off by one": ("visible = np.arange(L)[None, :] <= (P + t_of_row)[:, None]",
-                        "visible = np.arange(L)[None, :] < (P + t_of_row)[:, None]"),
-    "mask ignores past": ("visible = np.arange(L)[None, :] <= (P + t_of_row)[:, None]",
-                          "visible = np.arange(L)[None, :] <= (t_of_row)[:, None]"),
+    "mask off by one": ("vis = r <= pos", "vis = r < pos"),
+    "mask ignores past": ("visible_rows(P + t, L, window, n_sink) for t in t_of_row",
+                          "visible_rows(t, L, window, n_sink) for t in t_of_row"),
+    "window off by one": ("vis &= (r > pos - window) | (r < n_sink)", "vis &= (r >= pos - window) | (r < n_sink)"),
+    "sinks ignored": ("vis &= (r > pos - window) | (r < n_sink)", "vis &= (r > pos - window)"),
+    "learned sink ignored": ("w = w / (w.sum(axis=1, keepdims=True) + np.exp(sk - top))",
+                             "w = w / w.sum(axis=1, keepdims=True)"),
     "row order of score block": ("t_of_row = np.tile(np.arange(T), g)", "t_of_row = np.repeat(np.arange(T), g)"),
     "missing scale": ("s = (Q @ K.T) * scale", "s = (Q @ K.T)"),
     "keys not transposed": ("s = (Q @ K.T) * scale", "s = (Q @ K[:, ::-1].T) * scale"),
@@ -124,7 +127,39 @@ def pin_bruteforce(m):
                        atol=1e-12)
 
 
-PINS = [pin_complex_rotation, pin_frequencies, pin_position_offset, pin_torch_cast, pin_sdpa, pin_bruteforce]
+def pin_window_rows(m):
+    # hand-checked row set: position 9, window 3, two sinks
+    return np.flatnonzero(m.visible_rows(9, 12, window=3, n_sink=2)).tolist() == [0, 1, 7, 8, 9]
+
+
+def pin_window_slice(m):
+    # decode with window W equals plain attention over the last W rows
+    rng = np.random.default_rng(31)
+    q, kc, vc = rb(rng, (1, 4, 1, 8)), rb(rng, (1, 2, 24, 8)), rb(rng, (1, 2, 24, 8))
+    W, P = 5, 17
+    win = m.attend(q, kc, vc, np.array([P]), 2, window=W)
+    lo = P + 1 - W
+    sl = m.attend(q, kc[:, :, lo:], vc[:, :, lo:], np.array([W - 1]), 2)
+    return np.allclose(win, sl, rtol=0, atol=1e-12)
+
+
+def pin_sink_closed_form(m):
+    # equal keys: output = sum of the visible value rows / (rows + exp(sink - score))
+    rng = np.random.default_rng(37)
+    q, vc = rb(rng, (1, 2, 1, 8)), rb(rng, (1, 1, 12, 8))
+    kc = np.repeat(rb(rng, (1, 1, 1, 8)), 12, axis=2)
+    sinks = np.array([0.7, -0.4])
+    out = m.attend(q, kc, vc, np.array([7]), 1, sink_logits=sinks)
+    ok = True
+    for h in range(2):
+        s0 = float(f64(q[0, h, 0]) @ f64(kc[0, 0, 0])) / np.sqrt(8)
+        expect = f64(vc[0, 0, :8]).sum(axis=0) / (8 + np.exp(sinks[h] - s0))
+        ok &= np.allclose(out[0, h, 0], expect, rtol=0, atol=1e-12)
+    return ok
+
+
+PINS = [pin_complex_rotation, pin_frequencies, pin_position_offset, pin_torch_cast, pin_sdpa, pin_bruteforce,
+        pin_window_rows, pin_window_slice, pin_sink_closed_form]
 
 
 def test_unmodified_oracle_passes_every_pin():
