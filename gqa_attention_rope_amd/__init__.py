@@ -28,7 +28,9 @@ EXPORTED = (
     "gqa_rope_append",
     "gqa_decode_workspace_bytes",
     "gqa_decode_attn",
+    "gqa_decode_attn_ex",
     "gqa_prefill_attn",
+    "gqa_prefill_attn_ex",
     "gqa_status_string",
     "gqa_profile_enable",
     "gqa_profile_read",
@@ -38,6 +40,10 @@ EXPORTED = (
 )
 
 KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3}
+
+
+class GqaAttnOpts(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int), ("n_sink", ctypes.c_int), ("sink_logits", ctypes.c_void_p)]
 
 
 class GqaRopeParams(ctypes.Structure):
@@ -78,8 +84,14 @@ def lib():
     L.gqa_decode_workspace_bytes.restype = sz
     L.gqa_decode_attn.argtypes = [vp, vp, vp, vp, i32, vp, vp, sz, i32, i32, i32, i32, i32, f32, vp]
     L.gqa_decode_attn.restype = i32
+    L.gqa_decode_attn_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, sz, i32, i32, i32, i32, i32, f32,
+                                     ctypes.POINTER(GqaAttnOpts), vp]
+    L.gqa_decode_attn_ex.restype = i32
     L.gqa_prefill_attn.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, vp]
     L.gqa_prefill_attn.restype = i32
+    L.gqa_prefill_attn_ex.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
+                                      ctypes.POINTER(GqaAttnOpts), vp]
+    L.gqa_prefill_attn_ex.restype = i32
     L.gqa_status_string.argtypes = [i32]
     L.gqa_status_string.restype = ctypes.c_char_p
     L.gqa_profile_enable.argtypes = [i32]
@@ -186,9 +198,29 @@ def gqa_decode_workspace_bytes(B, n_q, n_kv, d, S):
     return int(lib().gqa_decode_workspace_bytes(B, n_q, n_kv, d, S))
 
 
+def _opts(window, n_sink, sink_logits, n_q, device):
+    """Options struct for the _ex entry points (None when every option is off)."""
+    import torch
+    if window < 0 or n_sink < 0:
+        raise ValueError("window and n_sink must be >= 0")
+    if not window and sink_logits is None:
+        return None, None
+    keep = None
+    ptr = None
+    if sink_logits is not None:
+        if not (isinstance(sink_logits, torch.Tensor) and sink_logits.dtype == torch.float32
+                and sink_logits.device.type == torch.device(device).type and sink_logits.is_contiguous()
+                and sink_logits.numel() == n_q):
+            raise ValueError(f"sink_logits must be a contiguous float32 device tensor of {n_q} values")
+        keep = sink_logits
+        ptr = sink_logits.data_ptr()
+    return GqaAttnOpts(int(window), int(n_sink), ptr), keep
+
+
 def gqa_decode_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, workspace=None, scale=0.0,
-                    stream=None):
-    """One new query per sequence attends to cache rows 0..past_len[b]; returns out [B, n_q, 1, d] bf16."""
+                    stream=None, window=0, n_sink=0, sink_logits=None):
+    """One new query per sequence attends to cache rows 0..past_len[b] (or its window and sinks);
+    returns out [B, n_q, 1, d] bf16."""
     import torch
     B, n_q, T, d = q_rot.shape
     if T != 1:
@@ -205,14 +237,18 @@ def gqa_decode_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, w
     if workspace is None:
         # the scheduling header at the start must be zero before first use
         workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q_rot.device)
-    _check(lib().gqa_decode_attn(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
-                                 _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B, n_q,
-                                 n_kv, d, S, float(scale), _stream(stream)))
+    opts, _keep = _opts(window, n_sink, sink_logits, n_q, q_rot.device)
+    _check(lib().gqa_decode_attn_ex(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
+                                    _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B,
+                                    n_q, n_kv, d, S, float(scale), ctypes.byref(opts) if opts else None,
+                                    _stream(stream)))
     return out
 
 
-def gqa_prefill_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, scale=0.0, stream=None):
-    """T new queries per sequence under the rectangular causal mask; returns out [B, n_q, T, d] bf16."""
+def gqa_prefill_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, scale=0.0, stream=None,
+                     window=0, n_sink=0, sink_logits=None):
+    """T new queries per sequence under the rectangular causal mask (and optional window / sinks);
+    returns out [B, n_q, T, d] bf16."""
     import torch
     B, n_q, T, d = q_rot.shape
     n_kv, S = k_cache.shape[1], k_cache.shape[2]
@@ -223,8 +259,10 @@ def gqa_prefill_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, 
     if out is None:
         out = torch.empty_like(q_rot)
     _bf16(out, "out", (B, n_q, T, d))
-    _check(lib().gqa_prefill_attn(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
-                                  _ptr(out), B, n_q, n_kv, T, d, S, float(scale), _stream(stream)))
+    opts, _keep = _opts(window, n_sink, sink_logits, n_q, q_rot.device)
+    _check(lib().gqa_prefill_attn_ex(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
+                                     _ptr(out), B, n_q, n_kv, T, d, S, float(scale),
+                                     ctypes.byref(opts) if opts else None, _stream(stream)))
     return out
 
 

@@ -119,10 +119,13 @@ size_t gqa_decode_workspace_bytes(int B, int n_q, int n_kv, int d, int S) {
     return gqa::decode_workspace_bytes(B, n_q, n_kv, d);
 }
 
-int gqa_decode_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
-                    int max_past_len, void* out, void* workspace, size_t workspace_bytes, int B, int n_q, int n_kv,
-                    int d, int S, float scale, void* stream) {
+int gqa_decode_attn_ex(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                       int max_past_len, void* out, void* workspace, size_t workspace_bytes, int B, int n_q, int n_kv,
+                       int d, int S, float scale, const gqa_attn_opts* opts, void* stream) {
     if (!q_rot || !k_cache || !v_cache || !past_len || !out || !workspace) return GQA_ERR_INVALID_ARG;
+    const gqa_attn_opts o = opts ? *opts : gqa_attn_opts{0, 0, nullptr};
+    if (o.window < 0 || o.n_sink < 0 || (o.sink_logits && (reinterpret_cast<uintptr_t>(o.sink_logits) & 3u)))
+        return GQA_ERR_INVALID_ARG;
     if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         !aligned16(workspace) || (reinterpret_cast<uintptr_t>(past_len) & 3u))
         return GQA_ERR_INVALID_ARG;
@@ -135,14 +138,25 @@ int gqa_decode_attn(const void* q_rot, const void* k_cache, const void* v_cache,
     hipError_t e = gqa::launch_decode(static_cast<const uint16_t*>(q_rot), static_cast<const uint16_t*>(k_cache),
                                       static_cast<const uint16_t*>(v_cache), past_len, max_past_len,
                                       static_cast<uint16_t*>(out), static_cast<float*>(workspace), B, n_q, n_kv, d,
-                                      S, resolve_scale(scale, d), g_decode_wg, static_cast<hipStream_t>(stream));
+                                      S, resolve_scale(scale, d), o.window, o.n_sink, o.sink_logits, g_decode_wg,
+                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GQA_OK : hip_status(e);
 }
 
-int gqa_prefill_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
-                     int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
-                     void* stream) {
+int gqa_decode_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                    int max_past_len, void* out, void* workspace, size_t workspace_bytes, int B, int n_q, int n_kv,
+                    int d, int S, float scale, void* stream) {
+    return gqa_decode_attn_ex(q_rot, k_cache, v_cache, past_len, max_past_len, out, workspace, workspace_bytes, B,
+                              n_q, n_kv, d, S, scale, nullptr, stream);
+}
+
+int gqa_prefill_attn_ex(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                        int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
+                        const gqa_attn_opts* opts, void* stream) {
     if (!q_rot || !k_cache || !v_cache || !past_len || !out) return GQA_ERR_INVALID_ARG;
+    const gqa_attn_opts o = opts ? *opts : gqa_attn_opts{0, 0, nullptr};
+    if (o.window < 0 || o.n_sink < 0 || (o.sink_logits && (reinterpret_cast<uintptr_t>(o.sink_logits) & 3u)))
+        return GQA_ERR_INVALID_ARG;
     if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         (reinterpret_cast<uintptr_t>(past_len) & 3u))
         return GQA_ERR_INVALID_ARG;
@@ -155,8 +169,15 @@ int gqa_prefill_attn(const void* q_rot, const void* k_cache, const void* v_cache
     hipError_t e = gqa::launch_prefill(static_cast<const uint16_t*>(q_rot), static_cast<const uint16_t*>(k_cache),
                                        static_cast<const uint16_t*>(v_cache), past_len, max_past_len,
                                        static_cast<uint16_t*>(out), B, n_q, n_kv, T, d, S, resolve_scale(scale, d),
-                                       static_cast<hipStream_t>(stream));
+                                       o.window, o.n_sink, o.sink_logits, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GQA_OK : hip_status(e);
+}
+
+int gqa_prefill_attn(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                     int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
+                     void* stream) {
+    return gqa_prefill_attn_ex(q_rot, k_cache, v_cache, past_len, max_past_len, out, B, n_q, n_kv, T, d, S, scale,
+                               nullptr, stream);
 }
 
 const char* gqa_status_string(int status) {

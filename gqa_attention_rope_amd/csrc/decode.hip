@@ -77,22 +77,55 @@ struct Cfg {
     static constexpr int LOADS = 2 * TILE * PPR / THREADS;  // 16-byte loads per thread per tile
 };
 
-__device__ __forceinline__ int tiles_of(const int32_t* past_len, int b, int pmax) {
+// Visible rows of the new query of a sequence with L = past_len + 1 cached
+// rows: all of them, or, under a sliding window of W rows, the sink rows
+// 0 .. n_sink-1 and the window rows w0 .. L-1 with w0 = L - W.  The tiles of
+// the segment are the nst sink tiles 0 .. nst-1 followed by the window tiles
+// at0, at0+1, .. (absolute 64-row tile indices); when the two ranges meet
+// (or there is no window) the tiles are simply 0 .. ceil(L/64)-1 and w0 = 0.
+struct Geo {
+    int nt;   // tiles of the segment
+    int nst;  // leading tiles (sinks, or all of them when contiguous)
+    int at0;  // absolute index of the first window tile
+    int w0;   // first visible window row (0 when every row is visible)
+};
+__device__ __forceinline__ Geo geo_of(int L, int window, int n_sink) {
+    Geo g;
+    const int all = (L + TILE - 1) / TILE;
+    if (window <= 0 || L - window <= n_sink) {
+        g.nt = all;
+        g.nst = all;
+        g.at0 = all;
+        g.w0 = 0;
+    } else {
+        g.w0 = L - window;
+        g.nst = (n_sink + TILE - 1) / TILE;
+        const int a0 = g.w0 / TILE;
+        g.at0 = a0 > g.nst ? a0 : g.nst;
+        g.nt = g.nst + all - g.at0;
+    }
+    return g;
+}
+__device__ __forceinline__ int rows_clamped(const int32_t* past_len, int b, int pmax) {
     int P = past_len[b];
     P = P < 0 ? 0 : (P > pmax ? pmax : P);
-    return (P + 1 + TILE - 1) / TILE;  // rows 0..P
+    return P + 1;  // rows 0..P
+}
+__device__ __forceinline__ int tiles_of(const int32_t* past_len, int b, int pmax, int window, int n_sink) {
+    return geo_of(rows_clamped(past_len, b, pmax), window, n_sink).nt;
 }
 
 // Exclusive prefix of per-sequence tile counts into s_pre[0..B], 256 sequences
 // per pass with one (clamped, unconditional) load per thread, so every pass
 // costs a single memory round trip.
-__device__ void tile_prefix(const int32_t* past_len, int B, int pmax, int* s_pre, int* s_wsum) {
+__device__ void tile_prefix(const int32_t* past_len, int B, int pmax, int window, int n_sink, int* s_pre,
+                            int* s_wsum) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     int carry = 0;
     for (int base = 0; base < B; base += THREADS) {
         const int b = base + tid;
-        const int n = tiles_of(past_len, b < B ? b : B - 1, pmax);
+        const int n = tiles_of(past_len, b < B ? b : B - 1, pmax, window, n_sink);
         const int mine = b < B ? n : 0;
         int x = mine;
 #pragma unroll
@@ -124,7 +157,8 @@ __device__ __forceinline__ long long owner_of(long long tau, long long T, long l
 // Position of one tile in the concatenated tile list: sequence b, segment sj
 // (= KV head * head chunks + chunk) inside it, tile tt inside the segment.
 struct Cursor {
-    int b, sj, tt, nt, L;
+    int b, sj, tt, nt, L;  // tt: index among the segment's nt tiles
+    int nst, at0, w0;      // the sequence's tile geometry (see geo_of)
 };
 
 // Byte offset in the LDS tile of 16-byte piece c of row R (rows of D bf16).
@@ -160,7 +194,8 @@ __device__ __forceinline__ Sched make_sched(int T_all, int static_pm, int chunk)
 
 // What one register stage holds (the same in every lane).
 struct Stage {
-    int tt, L;   // tile index inside its segment, valid rows of the segment
+    int tt, L;   // absolute 64-row tile index of the tile, rows of the segment
+    int w0;      // first visible window row of the segment (0: all rows visible)
     int slot;    // record slot of the piece the tile belongs to
     int flags;   // kind (TILE, BUBBLE = nothing loaded but work to come, END) | PIECE_END | GRABBED
 };
@@ -172,7 +207,7 @@ template <int D, int HGW, int NHG>
 __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ past_len, int pmax, float* __restrict__ ws, int B, int n_q, int n_kv, int S, int nhc,
-    float scale_log2, int static_pm, int chunk) {
+    float scale_log2, int static_pm, int chunk, int window, int n_sink) {
     using C = Cfg<D, HGW, NHG>;
     constexpr int KB = C::KB, KS = C::KS;
     constexpr int DPL = D / 64;                  // value dims each lane accumulates
@@ -188,7 +223,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     __shared__ int s_ticket;
     extern __shared__ int s_pre[];  // B + 1 entries
 
-    tile_prefix(past_len, B, pmax, s_pre, s_wsum);
+    tile_prefix(past_len, B, pmax, window, n_sink, s_pre, s_wsum);
 
     // values read from LDS are the same in every lane: keep them in scalar registers
     auto uni = [] __attribute__((always_inline)) (int x) { return __builtin_amdgcn_readfirstlane(x); };
@@ -225,6 +260,10 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         c.sj = uni(off / c.nt);
         c.tt = uni(off % c.nt);
         c.L = uni(rows_of(c.b));
+        const Geo gg = geo_of(c.L, window, n_sink);
+        c.nst = uni(gg.nst);
+        c.at0 = uni(gg.at0);
+        c.w0 = uni(gg.w0);
         return c;
     };
     auto advance = [&] __attribute__((always_inline)) (Cursor& c) {
@@ -235,13 +274,17 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         if (++c.b < B) {
             c.nt = uni(s_pre[c.b + 1] - s_pre[c.b]);
             c.L = uni(rows_of(c.b));
+            const Geo gg = geo_of(c.L, window, n_sink);
+            c.nst = uni(gg.nst);
+            c.at0 = uni(gg.at0);
+            c.w0 = uni(gg.w0);
         }
     };
 
     // ---- loader: the current range (static share first, then chunks) and at
     // most one ticket in flight or in hand
     Cursor ld;
-    ld.b = 0; ld.sj = 0; ld.tt = 0; ld.nt = 1; ld.L = 1;
+    ld.b = 0; ld.sj = 0; ld.tt = 0; ld.nt = 1; ld.L = 1; ld.nst = 1; ld.at0 = 1; ld.w0 = 0;
     const int tau_w = (int)share_begin(w, sc.Ts, G);
     int ld_left = (int)share_begin(w + 1, sc.Ts, G) - tau_w;
     int ld_rid = w;
@@ -281,8 +324,10 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         const bool tile = ld_left > 0;
         const int rem = tile ? ld_left - 1 : 0;
         const bool grab = !no_more && !have_next && !pending && rem <= 2;
-        stg.tt = uni(ld.tt);
+        const int at = ld.tt < ld.nst ? ld.tt : ld.at0 + (ld.tt - ld.nst);  // absolute tile of this one
+        stg.tt = uni(at);
         stg.L = uni(ld.L);
+        stg.w0 = uni(ld.w0);
         stg.slot = uni(ld_rid + ld.b * segs_per_b + ld.sj);
         stg.flags = uni((tile ? K_TILE : ((no_more && !pending) ? K_END : K_BUBBLE)) |
                         ((ld_left == 1 || ld.tt + 1 == ld.nt) ? F_PIECE_END : 0) | (grab ? F_GRABBED : 0));
@@ -300,7 +345,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
             __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg_off), (short)0, valid_bytes, RSRC_FLAGS);
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg_off), (short)0, valid_bytes, RSRC_FLAGS);
-        const int soff = uni(ld.tt * TILEB);
+        const int soff = uni(at * TILEB);
 #pragma unroll
         for (int x = 0; x < HALF; ++x) {
             buf[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + x * THREADS * 16, 0);
@@ -424,8 +469,9 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const int pv_base1 = D == 128 ? lds_byte<D>(rbase + 2, lane >> 2) + (lane & 3) * 4 - 2 * ROWB : pv_base0;
 
     // ---- one tile: q.k on MFMA, online softmax, weighted value sum (this wave's rows and heads)
-    // vrows: rows of the tile inside the segment's valid range (1..64)
-    auto compute_tile = [&] __attribute__((always_inline)) (int vrows) {
+    // vrows: rows of the tile below L (1..64); wrow: rows of the tile below the
+    // window start w0 are hidden unless they are sinks (absolute row < n_sink)
+    auto compute_tile = [&] __attribute__((always_inline)) (int vrows, int row0, int w0) {
         // S^T = K Q^T: A = 16 K rows x 32 dims (lane: row l16, dims 8 lq + 0..7), B = Q^T
         f32x4_t sacc[KB];
 #pragma unroll
@@ -446,7 +492,8 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool valid = rbase + 16 * kb + 4 * lq + i < vrows;
+                const int rr = rbase + 16 * kb + 4 * lq + i;
+                const bool valid = rr < vrows && (row0 + rr >= w0 || row0 + rr < n_sink);
                 sc[kb][i] = valid ? sacc[kb][i] * scale_log2 : -INFINITY;
                 tm = fmaxf(tm, sc[kb][i]);
             }
@@ -551,7 +598,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         if (seg_start) load_qop();
         issue(buf, qbuf, tkbuf, stg);
         if ((cs.flags & KIND_MASK) == K_TILE) {
-            compute_tile(cs.L - cs.tt * TILE);
+            compute_tile(cs.L - cs.tt * TILE, cs.tt * TILE, cs.w0);
             seg_start = (cs.flags & F_PIECE_END) != 0;
             if (seg_start) {
                 park();
@@ -588,7 +635,8 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
                                                                         const int32_t* __restrict__ past_len,
                                                                         int pmax, uint16_t* __restrict__ out, int B,
                                                                         int n_q, int n_kv, int nhc, int gc, int G,
-                                                                        int static_pm, int chunk) {
+                                                                        int static_pm, int chunk, int window,
+                                                                        int n_sink, const float* sink_logits) {
     constexpr int DPL = D / 64;  // dims per lane
     constexpr int REC = D + 4;
     constexpr int RB = 8;        // records per wave and batch
@@ -605,7 +653,7 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
     long long pre_b = 0, total = 0;
     for (int base = 0; base < B; base += 64) {
         const int bb = base + lane;
-        const int n = bb < B ? tiles_of(past_len, bb, pmax) : 0;
+        const int n = bb < B ? tiles_of(past_len, bb, pmax, window, n_sink) : 0;
         int before = (bb < b) ? n : 0;
         int all = n;
 #pragma unroll
@@ -616,7 +664,7 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
         pre_b += before;
         total += all;
     }
-    const int nt_b = tiles_of(past_len, b, pmax);
+    const int nt_b = tiles_of(past_len, b, pmax, window, n_sink);
 
     const int j = h / g, hh = h % g, hc = hh / gc, hl = hh % gc;
     const long long segs_per_b = (long long)n_kv * nhc;
@@ -688,10 +736,13 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
     if (lane == 0) s_ml[wave] = make_float2(M, L);
     __syncthreads();
     if (wave != 0) return;
-    float Mt = -INFINITY;
+    // a learned sink logit (natural units, like the scaled scores) joins the
+    // normaliser as one more term with no value
+    const float sk = sink_logits ? sink_logits[h] * LOG2E : -INFINITY;
+    float Mt = sk;
 #pragma unroll
     for (int k = 0; k < CMB_WAVES; ++k) Mt = fmaxf(Mt, s_ml[k].x);
-    float Lt = 0.f, o[DPL];
+    float Lt = sk == -INFINITY ? 0.f : fast_exp2(sk - Mt), o[DPL];
 #pragma unroll
     for (int x = 0; x < DPL; ++x) o[x] = 0.f;
 #pragma unroll
@@ -715,10 +766,11 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
 template <int D, int HGW, int NHG>
 hipError_t launch_partial_t(int G, const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                             const int32_t* past_len, int pmax, float* ws, int B, int n_q, int n_kv, int S, int nhc,
-                            float scale_log2, int static_pm, int chunk, hipStream_t st) {
+                            float scale_log2, int static_pm, int chunk, int window, int n_sink, hipStream_t st) {
     const size_t dyn = (size_t)(B + 1) * sizeof(int);
     hipLaunchKernelGGL((decode_partial_kernel<D, HGW, NHG>), dim3(G), dim3(THREADS), dyn, st, q_rot, k_cache,
-                       v_cache, past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2, static_pm, chunk);
+                       v_cache, past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2, static_pm, chunk, window,
+                       n_sink);
     return hipGetLastError();
 }
 
@@ -733,7 +785,7 @@ int occupancy_t(int B) {
 
 using occ_fn = int (*)(int);
 using partial_fn = hipError_t (*)(int, const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int, float*,
-                                  int, int, int, int, int, float, int, int, hipStream_t);
+                                  int, int, int, int, int, float, int, int, int, int, hipStream_t);
 
 struct Variant {
     int hgw, nhg;
@@ -791,7 +843,8 @@ size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d) {
 
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
-                         int n_kv, int d, int S, float scale, int wg_override, hipStream_t st) {
+                         int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
+                         int wg_override, hipStream_t st) {
     const DecodePlan p = decode_plan(n_q, n_kv, d);
     const Variant& v = pick_variant(n_q / n_kv);
 
@@ -832,17 +885,19 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
 
         prof_begin(K_DECODE_PARTIAL, st);
         hipError_t e = (d == 128 ? v.fn128 : v.fn64)(G, q, kc, vc, pl, max_past_len, ws, nb, n_q, n_kv, S, p.nhc,
-                                                     scale_log2, spm, (int)chunk, st);
+                                                     scale_log2, spm, (int)chunk, window, n_sink, st);
         prof_end(K_DECODE_PARTIAL, st);
         if (e != hipSuccess) return e;
 
         prof_begin(K_DECODE_COMBINE, st);
         if (d == 128)
-            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl, max_past_len, o,
-                               nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk);
+            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl,
+                               max_past_len, o, nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk, window, n_sink,
+                               sink_logits);
         else
-            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl, max_past_len, o,
-                               nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk);
+            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl,
+                               max_past_len, o, nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk, window, n_sink,
+                               sink_logits);
         prof_end(K_DECODE_COMBINE, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -55,11 +55,13 @@ size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d);
 void set_decode_schedule(int static_permille, int chunk_tiles);
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
-                         int n_kv, int d, int S, float scale, int wg_override, hipStream_t st);
+                         int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
+                         int wg_override, hipStream_t st);
 
 // ---- prefill -----------------------------------------------------------------------
 hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                           const int32_t* past_len, int max_past_len, uint16_t* out, int B, int n_q, int n_kv, int T,
-                          int d, int S, float scale, hipStream_t st);
+                          int d, int S, float scale, int window, int n_sink, const float* sink_logits,
+                          hipStream_t st);
 
 }  // namespace gqa

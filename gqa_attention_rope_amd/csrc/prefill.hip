@@ -46,7 +46,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ v_cache,
                                                           const int32_t* __restrict__ past_len, int pmax,
                                                           uint16_t* __restrict__ out, int n_q, int n_kv, int T,
-                                                          int S, int hpw, int tq, int n_tq, float scale_log2) {
+                                                          int S, int hpw, int tq, int n_tq, float scale_log2,
+                                                          int window, int n_sink, const float* sink_logits) {
     constexpr int PPR = D / 8;     // 16-byte pieces per key row
     constexpr int KS = D / 32;     // MFMA k-steps over d
     constexpr int DB = D / 16;     // 16-dim blocks of the output
@@ -80,7 +81,20 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
     const int t_hi = (t0 + tq < T ? t0 + tq : T) - 1;
     const int kv_end = P + t_hi + 1;            // keys visible to the last row of this workgroup
     const int n_tiles = (kv_end + KT - 1) / KT;
-    const int first_masked_tile = (P + t0 + 1) / KT;  // tiles before this one are fully visible
+    const int first_masked_tile = (P + t0 + 1) / KT;  // tiles before this one are fully visible (no window)
+    // Under a sliding window, tiles wholly after the sink rows and before the
+    // first row's window start (the earliest of this workgroup) hold no visible
+    // key: the loop runs over the nst sink tiles, then from tile wt0 on.
+    int nst = n_tiles, wt0 = n_tiles;
+    if (window > 0) {
+        const int ws0 = P + t0 - window + 1;  // first visible window key of row t0
+        if (ws0 > n_sink) {
+            nst = (n_sink + KT - 1) / KT;
+            const int a0 = ws0 / KT;
+            wt0 = a0 > nst ? a0 : nst;
+        }
+    }
+    const int n_iter = nst < n_tiles ? nst + (n_tiles - wt0) : n_tiles;
 
     // ---- Q^T operand: 8 dims of one query row per lane and k-step
     bf16x8_t qop[2][KS];
@@ -155,12 +169,14 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-    load(0);
-    for (int tile = 0; tile < n_tiles; ++tile) {
+    auto tile_of = [&](int it) { return it < nst ? it : wt0 + (it - nst); };
+    load(tile_of(0));
+    for (int it = 0; it < n_iter; ++it) {
+        const int tile = tile_of(it);
         __syncthreads();
         store();
         __syncthreads();
-        if (tile + 1 < n_tiles) load(tile + 1);
+        if (it + 1 < n_iter) load(tile_of(it + 1));
 
         // ---- S^T = K Q^T for 64 keys x 32 query rows
         f32x4_t sacc[4][2];
@@ -179,15 +195,18 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
 
         // ---- mask (only tiles that cross a row's causal bound), online softmax per query row
         const int key0 = tile * KT;
-        if (tile >= first_masked_tile) {
+        if (tile >= first_masked_tile || window > 0) {
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 const int lim = P + row_t[nb];  // last visible key of this row
+                const int wlo = window > 0 ? lim - window : -1;  // keys at or below it left the window
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (key0 + 16 * mb + 4 * lq + i > lim) sacc[mb][nb][i] = -INFINITY;
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = key0 + 16 * mb + 4 * lq + i;
+                        if (key > lim || (key <= wlo && key >= n_sink)) sacc[mb][nb][i] = -INFINITY;
+                    }
             }
         }
         // [hi/lo][kb][nb]: the weights as PV B operands, split p = hi + lo with both parts
@@ -204,18 +223,20 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
             // The exponent reference m_ref (scaled, base 2) only moves when the row
             // maximum exceeds it by more than 8: weights then stay below 2^8, and
             // the accumulators are rescaled rarely instead of on every tile.
-            const float mxs = mx * scale_log2;  // finite: key 0 is visible to every row
+            const float mxs = mx * scale_log2;
             const bool move = mxs > m_run[nb] + 8.f;
             const float mn = move ? mxs : m_run[nb];
             const float alpha = move ? fast_exp2(m_run[nb] - mn) : 1.f;
             m_run[nb] = mn;
+            // a row that has seen no key yet (possible under a window) keeps weight 0
+            const float mref = mn == -INFINITY ? 0.f : mn;
             float ps = 0.f;
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(__builtin_fmaf(sacc[mb][nb][i], scale_log2, -mn));
+                    p[i] = fast_exp2(__builtin_fmaf(sacc[mb][nb][i], scale_log2, -mref));
                     ps += p[i];
                 }
                 const uint32_t h01 = cvt_pk_bf16(p[0], p[1]), h23 = cvt_pk_bf16(p[2], p[3]);
@@ -264,6 +285,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         l += __shfl_xor(l, 16, 64);
         l += __shfl_xor(l, 32, 64);
         if (!row_ok[nb]) continue;
+        // a learned sink logit joins the normaliser (same exponent reference as the weights)
+        if (sink_logits) l += fast_exp2(sink_logits[row_h[nb]] * LOG2E_P - m_run[nb]);
         const float inv = 1.f / l;
         uint16_t* dst = out + ((size_t)b * n_q * T + (size_t)row_h[nb] * T + row_t[nb]) * D;
 #pragma unroll
@@ -279,7 +302,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
 
 hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                           const int32_t* past_len, int max_past_len, uint16_t* out, int B, int n_q, int n_kv, int T,
-                          int d, int S, float scale, hipStream_t st) {
+                          int d, int S, float scale, int window, int n_sink, const float* sink_logits,
+                          hipStream_t st) {
     const int g = n_q / n_kv;
     const int hpw = g < ROWS ? g : ROWS;  // heads per workgroup
     const int tq = ROWS / hpw;            // positions per workgroup
@@ -294,10 +318,11 @@ hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const 
         if (d == 128)
             hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(NTHR), 0, st, q_rot + qo, k_cache + co,
                                v_cache + co, past_len + b0, max_past_len, out + qo, n_q, n_kv, T, S, hpw, tq, n_tq,
-                               scale_log2);
+                               scale_log2, window, n_sink, sink_logits);
         else
             hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(NTHR), 0, st, q_rot + qo, k_cache + co, v_cache + co,
-                               past_len + b0, max_past_len, out + qo, n_q, n_kv, T, S, hpw, tq, n_tq, scale_log2);
+                               past_len + b0, max_past_len, out + qo, n_q, n_kv, T, S, hpw, tq, n_tq, scale_log2,
+                               window, n_sink, sink_logits);
         prof_end(K_PREFILL, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

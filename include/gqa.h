@@ -163,6 +163,39 @@ int gqa_prefill_attn(const void* q_rot, const void* k_cache, const void* v_cache
                      int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
                      void* stream);
 
+/*
+ * Attention options ([P7] "Part 7: The Modern Decoder Block", modules L7.5
+ * and L7.7, name the sliding window, StreamingLLM sinks and learned sinks; the
+ * pages give no formula, the rules below are the plainest reading):
+ *   window       > 0: the query at position p sees cache rows p - window + 1
+ *                .. p only (its own row and the window - 1 before it), plus
+ *                the sinks; 0: no window (every row 0 .. p).
+ *   n_sink       under a window, rows 0 .. n_sink - 1 stay visible to every
+ *                query.  Ignored without a window.
+ *   sink_logits  NULL, or a device fp32 array [n_q]: one learned logit per
+ *                query head, in the units of the scaled scores q.k * scale;
+ *                it joins the softmax normaliser as one more term and carries
+ *                no value (4-byte aligned).
+ * With the _ex entry points the decode kernel visits only the tiles holding
+ * visible rows, so a window makes the KV read O(window); the prefill kernel
+ * skips tiles that lie wholly between the sinks and the earliest window.
+ */
+typedef struct gqa_attn_opts {
+    int window;
+    int n_sink;
+    const float* sink_logits;
+} gqa_attn_opts;
+
+/* gqa_decode_attn / gqa_prefill_attn with options (NULL = none, the plain
+ * entry points); same arguments, layouts and errors otherwise, plus
+ * INVALID_ARG for a negative window or n_sink or a misaligned sink_logits. */
+int gqa_decode_attn_ex(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                       int max_past_len, void* out, void* workspace, size_t workspace_bytes, int B, int n_q, int n_kv,
+                       int d, int S, float scale, const gqa_attn_opts* opts, void* stream);
+int gqa_prefill_attn_ex(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                        int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
+                        const gqa_attn_opts* opts, void* stream);
+
 /* Human-readable text for a status code; for GQA_ERR_HIP it includes the
  * last HIP error message recorded by this thread.  Never NULL. */
 const char* gqa_status_string(int status);

@@ -149,3 +149,64 @@ def test_decode_schedule_override_validates():
         with pytest.raises(ValueError):
             gq.gqa_set_decode_schedule(*bad)
     gq.gqa_set_decode_schedule()  # defaults
+
+
+def opts(window=0, n_sink=0, sink=None):
+    return gq.GqaAttnOpts(window, n_sink, sink)
+
+
+def decode_ex(o, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, pl=FAKE, maxp=10, out=FAKE, ws=FAKE, wsb=1 << 40, B=2, n_q=8, n_kv=2, d=128,
+             S=64, scale=0.0)
+    a.update(kw)
+    return gq.lib().gqa_decode_attn_ex(P(a["q"]), P(a["kc"]), P(a["vc"]), P(a["pl"]), a["maxp"], P(a["out"]),
+                                       P(a["ws"]), a["wsb"], a["B"], a["n_q"], a["n_kv"], a["d"], a["S"], a["scale"],
+                                       None if o is None else ctypes.byref(o), None)
+
+
+def prefill_ex(o, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, pl=FAKE, maxp=10, out=FAKE, B=2, n_q=8, n_kv=2, T=4, d=128, S=64, scale=0.0)
+    a.update(kw)
+    return gq.lib().gqa_prefill_attn_ex(P(a["q"]), P(a["kc"]), P(a["vc"]), P(a["pl"]), a["maxp"], P(a["out"]),
+                                        a["B"], a["n_q"], a["n_kv"], a["T"], a["d"], a["S"], a["scale"],
+                                        None if o is None else ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize("o", [opts(window=-1), opts(n_sink=-3), opts(window=8, sink=FAKE + 2)])
+def test_attention_options_validation(o):
+    assert decode_ex(o) == INV
+    assert prefill_ex(o) == INV
+
+
+def test_attention_options_shape_checks_still_apply():
+    o = opts(window=16, n_sink=4, sink=FAKE)
+    assert decode_ex(o, n_q=8, n_kv=3) == GRP
+    assert prefill_ex(o, d=80) == HD
+    assert decode_ex(o, q=0) == INV
+
+
+def test_attention_options_accepted_without_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    for o in (None, opts(), opts(window=16, n_sink=4), opts(window=1, sink=FAKE)):
+        assert decode_ex(o) == HIP
+        assert prefill_ex(o) == HIP
+
+
+def test_python_binding_validates_attention_options():
+    import torch
+    assert gq._opts(0, 0, None, 8, "cpu") == (None, None)
+    o, _ = gq._opts(64, 4, None, 8, "cpu")
+    assert (o.window, o.n_sink, o.sink_logits) == (64, 4, None)
+    sk = torch.zeros(8)
+    o, keep = gq._opts(0, 0, sk, 8, "cpu")
+    assert o.sink_logits == sk.data_ptr() and keep is sk
+    for bad in (dict(window=-1), dict(n_sink=-1), dict(window=0, n_sink=-2),
+                dict(sink_logits=torch.zeros(3)),                        # one logit per query head
+                dict(sink_logits=torch.zeros(8, dtype=torch.float64)),   # float32 only
+                dict(sink_logits=torch.zeros(16)[::2])):                 # contiguous only
+        a = dict(window=16, n_sink=0, sink_logits=None)
+        a.update(bad)
+        with pytest.raises(ValueError):
+            gq._opts(a["window"], a["n_sink"], a["sink_logits"], 8, "cpu")

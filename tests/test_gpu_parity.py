@@ -345,3 +345,63 @@ def test_full_size_chunked_prefill():
     q_ref, kc_ref, vc_ref = rope_append(q_s, kn_s, vn_s, kc_s, vc_s, past[sb], w["theta"])
     ref = attend(q_ref, kc_ref, vc_ref, past[sb], n_kv)
     check_out(synth.bits(out[sb]), ref, "chunked prefill")
+
+
+# ---------------------------------------------------------------- sliding window, sinks, learned sinks
+
+WINDOW_DECODE_CASES = [
+    # B, n_q, n_kv, d, S, past, window, n_sink, learned sinks
+    (4, 32, 8, 128, 3000, [2999, 0, 700, 1500], 256, 0, False),
+    (4, 32, 8, 128, 3000, [2999, 0, 700, 1500], 100, 4, True),
+    (4, 32, 8, 128, 3000, [2999, 10, 700, 1500], 1000, 130, False),  # sinks span three tiles
+    (3, 64, 8, 128, 600, [511, 300, 599], 1, 0, False),              # one-row window, g = 8
+    (2, 6, 2, 64, 300, [299, 77], 64, 64, True),                      # window meets the sinks
+    (2, 6, 2, 64, 300, [299, 77], 5000, 0, True),                     # window wider than the context
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_DECODE_CASES,
+                         ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}d{c[3]}W{c[6]}ns{c[7]}{'L' if c[8] else ''}")
+def test_decode_window_and_sinks(case):
+    B, n_q, n_kv, d, S, past, W, NS, learned = case
+    say(f"decode window {case}")
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=1100 + W)
+    for b in range(B):  # row past_len is attended: make it finite
+        kc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 1200 + b))
+        vc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 1300 + b))
+    sinks = np.random.default_rng(W + NS).standard_normal(n_q).astype(np.float32) if learned else None
+    ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    sk = torch.from_numpy(sinks).to(DEV) if learned else None
+    for sched in ((-1, 0), (0, 1), (1000, 2)):
+        gq.gqa_set_decode_schedule(*sched)
+        try:
+            out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), window=W, n_sink=NS,
+                                     sink_logits=sk)
+            torch.cuda.synchronize()
+        finally:
+            gq.gqa_set_decode_schedule()
+        check_out(synth.bits(out), ref, f"decode window {W} sinks {NS} schedule {sched}")
+
+
+WINDOW_PREFILL_CASES = [
+    # B, n_q, n_kv, T, d, S, past, window, n_sink, learned sinks
+    (2, 8, 2, 33, 128, 400, [20, 200], 50, 4, False),
+    (2, 8, 2, 70, 128, 400, [0, 257], 64, 0, True),
+    (1, 32, 8, 130, 128, 600, [300], 1, 0, False),
+    (2, 6, 2, 40, 64, 300, [100, 3], 17, 70, True),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_PREFILL_CASES,
+                         ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}T{c[3]}d{c[4]}W{c[7]}ns{c[8]}{'L' if c[9] else ''}")
+def test_prefill_window_and_sinks(case):
+    B, n_q, n_kv, T, d, S, past, W, NS, learned = case
+    say(f"prefill window {case}")
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=1400 + W)
+    sinks = np.random.default_rng(3 * W + NS).standard_normal(n_q).astype(np.float32) if learned else None
+    ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    sk = torch.from_numpy(sinks).to(DEV) if learned else None
+    out = gq.gqa_prefill_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), window=W, n_sink=NS,
+                              sink_logits=sk)
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, f"prefill window {W} sinks {NS}")
