@@ -5,9 +5,9 @@ anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may use it.  It shares no code, constants
 or helpers with the HIP library in ``gqa_attention_rope_amd/``.
 
-Parity status of each function is stated in its docstring; the one function
-whose values no page fixes (the blend band of Llama-3 scaled RoPE) says
-"parity unpinned".
+Parity status of each function is stated in its docstring; the functions
+whose values no page fixes (the blend band of Llama-3 scaled RoPE and the ramp
+of YaRN) say "parity unpinned".
 """
 
 from .gqa_oracle import (  # noqa: F401
@@ -16,7 +16,10 @@ from .gqa_oracle import (  # noqa: F401
     f64_to_bf16,
     rope_frequencies,
     llama3_scaled_frequencies,
+    yarn_frequencies,
+    rope_attention_factor,
     rotate_pairs,
+    rope_rotate,
     rope_append,
     attend,
     attend_bruteforce,

@@ -27,8 +27,19 @@ Parity status:
                               formula.  Only its limits are pinned (factor 1 is
                               the identity, short wavelengths untouched,
                               longest ones divided by the factor, continuity).
+  rope_frequencies linear     pinned (PI = plain RoPE at position p / s)
+  rope_frequencies ntk        pinned (freq_0 = 1, lowest frequency divided by
+                              exactly s, geometric progression)
+  yarn_frequencies            PARITY UNPINNED in the ramp (the pages only name
+                              YaRN); pinned: both limits, continuity, and it
+                              agrees with the separately written Llama-3 rule
+                              when given the same cutoffs
+  rope_attention_factor       pinned (closed form 0.1 ln s + 1; equal-position
+                              q.k scales by its square)
   rotate_pairs / rope_append  pinned (complex multiplication, p = 0 identity,
-                              relative-offset invariance, index rule, sizes)
+                              relative-offset invariance, index rule, sizes);
+                              partial rotary pinned by reduction to full RoPE
+                              of the leading dims and a bit-exact tail
   visible_rows (window, sinks) pinned by reduction to the full mask (window at
                               least the context, sinks covering it), the
                               one-row window (the output is that value row),
@@ -102,21 +113,54 @@ def f64_to_bf16(x):
 # ---------------------------------------------------------------------------
 
 
-def rope_frequencies(theta, d, scaling=None):
-    """Per-pair rotary frequencies freq_i = theta ** (-2 i / d), i = 0 .. d/2-1.
+SCALING_KINDS = ("llama3", "linear", "ntk", "yarn")
+
+
+def rope_frequencies(theta, d, scaling=None, rotary_dim=None):
+    """Per-pair rotary frequencies freq_i = theta ** (-2 i / r), i = 0 .. r/2-1.
 
     [KV] section "RoPE has to know where it is": the frequency of pair i is
-    theta raised to minus (2i / head_dim).  With ``scaling`` (a dict with
-    factor, low_freq_factor, high_freq_factor, original_max_pos) the Llama-3
-    rule below is applied afterwards ([KV] "Training details that matter"
-    names the fields; [P7] module L7.4 lists Llama-3 scaling).
+    theta raised to minus (2i / head_dim).  r is the number of rotated dims:
+    the head dimension d, or ``rotary_dim`` < d for partial rotary ([P7]
+    module L7.3 names it; reading taken: the exponent uses r, as when the
+    first r dims formed a head of their own).
+
+    ``scaling`` (a dict) selects a context-extension rule ([P7] module L7.4
+    lists PI, NTK, YaRN and Llama-3 scaling; the pages print none of the
+    formulas, so each follows its published definition):
+      type "llama3" (the default when no type is given): factor,
+          low_freq_factor, high_freq_factor, original_max_pos; see
+          ``llama3_scaled_frequencies``.  [KV] "Training details that matter"
+          names these fields.
+      type "linear" (position interpolation, Chen et al. 2023): positions are
+          divided by ``factor``, i.e. every frequency is.
+      type "ntk" (NTK-aware base change): the base becomes
+          theta * factor ** (r / (r - 2)), which leaves freq_0 = 1 and divides
+          the lowest frequency by exactly ``factor``.
+      type "yarn" (Peng et al. 2023, the YaRN paper the course cites): factor,
+          beta_slow (alpha), beta_fast (beta), original_max_pos; see
+          ``yarn_frequencies``.  Its attention factor is applied by
+          ``rope_rotate``.
     """
-    if d % 2:
-        raise ValueError("head dimension must be even")
-    i = np.arange(d // 2, dtype=np.float64)
-    freq = np.power(float(theta), -(2.0 * i) / d)
-    if scaling is not None:
-        freq = llama3_scaled_frequencies(freq, **scaling)
+    r = d if rotary_dim is None else int(rotary_dim)
+    if r % 2 or not 0 < r <= d:
+        raise ValueError("rotary_dim must be even and in (0, d]")
+    kind = None if scaling is None else scaling.get("type", "llama3")
+    if kind is not None and kind not in SCALING_KINDS:
+        raise ValueError(f"unknown RoPE scaling {kind!r}")
+    base = float(theta)
+    if kind == "ntk":
+        base = base * float(scaling["factor"]) ** (r / (r - 2.0))
+    i = np.arange(r // 2, dtype=np.float64)
+    freq = np.power(base, -(2.0 * i) / r)
+    if kind == "llama3":
+        freq = llama3_scaled_frequencies(freq, scaling["factor"], scaling["low_freq_factor"],
+                                         scaling["high_freq_factor"], scaling["original_max_pos"])
+    elif kind == "linear":
+        freq = freq / float(scaling["factor"])
+    elif kind == "yarn":
+        freq = yarn_frequencies(freq, scaling["factor"], scaling.get("beta_slow", 1.0),
+                                scaling.get("beta_fast", 32.0), scaling["original_max_pos"])
     return freq
 
 
@@ -149,6 +193,40 @@ def llama3_scaled_frequencies(freq, factor, low_freq_factor, high_freq_factor, o
     return out
 
 
+def yarn_frequencies(freq, factor, alpha, beta, original_max_pos):
+    """YaRN's "NTK-by-parts" frequencies.  PARITY UNPINNED in the ramp.
+
+    Following the YaRN paper's definition (the pages cite the paper and name
+    the method, nothing more): rho = original_max_pos / lambda counts the
+    turns pair i makes over the original context.  A ramp gamma(rho) is 0 for
+    rho < alpha, 1 for rho > beta and (rho - alpha) / (beta - alpha) between;
+    the new frequency is (1 - gamma) freq / factor + gamma freq, so pairs that
+    turn many times keep their frequency and pairs that turn less than alpha
+    times are interpolated fully.
+    """
+    freq = np.asarray(freq, dtype=np.float64)
+    rho = original_max_pos * freq / (2.0 * math.pi)
+    gamma = np.clip((rho - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * freq / factor + gamma * freq
+
+
+def rope_attention_factor(scaling):
+    """Multiplier of the rotated dims: YaRN's attention temperature, else 1.
+
+    The YaRN paper scales the logits by 1/t with sqrt(1/t) = 0.1 ln(s) + 1;
+    multiplying both the rotated q and the rotated k by sqrt(1/t) does that.
+    ``attn_factor`` in ``scaling``, when given and > 0, replaces the default.
+    """
+    if scaling is None:
+        return 1.0
+    given = float(scaling.get("attn_factor", 0.0) or 0.0)
+    if given > 0.0:
+        return given
+    if scaling.get("type", "llama3") == "yarn":
+        return 0.1 * math.log(float(scaling["factor"])) + 1.0
+    return 1.0
+
+
 def rotate_pairs(x, angle, layout="interleaved"):
     """Rotate each (a, b) pair of the last axis of ``x`` by ``angle``.
 
@@ -178,15 +256,36 @@ def rotate_pairs(x, angle, layout="interleaved"):
     return out
 
 
-def rope_append(q, k_new, v_new, k_cache, v_cache, past_len, theta, layout="interleaved", scaling=None):
+def rope_rotate(x, pos, theta, layout="interleaved", scaling=None, rotary_dim=None):
+    """fp64 RoPE of the last axis of ``x`` (values, not bits) at positions ``pos``.
+
+    The first r dims (r = rotary_dim or d) turn pair by pair by pos * freq_i
+    and are multiplied by the attention factor; dims r .. d-1 pass through
+    unchanged ([P7] module L7.3 "partial rotary"; reading taken: the half
+    layout pairs dim i with i + r/2 inside the rotated part).  ``pos`` has the
+    shape of x without its last axis, or broadcasts to it.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    r = d if rotary_dim is None else int(rotary_dim)
+    freq = rope_frequencies(theta, d, scaling, r)
+    angle = np.asarray(pos, dtype=np.float64)[..., None] * freq
+    out = np.array(x, copy=True)
+    out[..., :r] = rotate_pairs(x[..., :r], angle, layout) * rope_attention_factor(scaling)
+    return out
+
+
+def rope_append(q, k_new, v_new, k_cache, v_cache, past_len, theta, layout="interleaved", scaling=None,
+                rotary_dim=None):
     """RoPE on q and the new k at offset past_len, then write k_rot and v into the cache.
 
     [KV] "RoPE has to know where it is": new token t of a sequence with
     past_len cached rows sits at position past_len + t.
     [ATL] cache formula: the call writes cache rows past_len .. past_len+T-1
     with the rotated keys and the values; the keys are stored after rotation.
-    All other rows keep their contents.  q_rot and k_rot are rounded to bf16
-    once, from fp64; v is copied bit for bit.
+    All other rows keep their contents.  The rotated dims of q_rot and k_rot
+    are rounded to bf16 once, from fp64; dims beyond rotary_dim and v are
+    copied bit for bit.
 
     Returns (q_rot, k_cache_out, v_cache_out) as new uint16 arrays.
     """
@@ -195,17 +294,19 @@ def rope_append(q, k_new, v_new, k_cache, v_cache, past_len, theta, layout="inte
     v_new = np.asarray(v_new, dtype=np.uint16)
     B, n_q, T, d = q.shape
     S = k_cache.shape[2]
-    freq = rope_frequencies(theta, d, scaling)
-    q_rot = np.empty_like(q)
+    r = d if rotary_dim is None else int(rotary_dim)
+    q_rot = np.array(q, copy=True)
     kc = np.array(k_cache, dtype=np.uint16, copy=True)
     vc = np.array(v_cache, dtype=np.uint16, copy=True)
     for b in range(B):
         pos = int(past_len[b]) + np.arange(T, dtype=np.float64)
         if int(past_len[b]) < 0 or int(past_len[b]) + T > S:
             raise ValueError("past_len + T exceeds the cache")
-        angle = pos[:, None] * freq[None, :]  # [T, d/2]
-        q_rot[b] = f64_to_bf16(rotate_pairs(bf16_to_f64(q[b]), angle[None], layout))
-        k_rot = f64_to_bf16(rotate_pairs(bf16_to_f64(k_new[b]), angle[None], layout))
+        qr = rope_rotate(bf16_to_f64(q[b]), pos[None, :], theta, layout, scaling, r)
+        kr = rope_rotate(bf16_to_f64(k_new[b]), pos[None, :], theta, layout, scaling, r)
+        q_rot[b][..., :r] = f64_to_bf16(qr[..., :r])
+        k_rot = np.array(k_new[b], copy=True)
+        k_rot[..., :r] = f64_to_bf16(kr[..., :r])
         rows = int(past_len[b]) + np.arange(T)
         kc[b][:, rows, :] = k_rot
         vc[b][:, rows, :] = v_new[b]

@@ -25,8 +25,18 @@ MUTANTS = {
     "half pairing": ("a, b = x[..., : d // 2], x[..., d // 2:]", "a, b = x[..., d // 2:], x[..., : d // 2]"),
     "no position offset": ("pos = int(past_len[b]) + np.arange(T, dtype=np.float64)",
                            "pos = np.arange(T, dtype=np.float64)"),
-    "frequency exponent": ("freq = np.power(float(theta), -(2.0 * i) / d)",
-                           "freq = np.power(float(theta), -(1.0 * i) / d)"),
+    "frequency exponent": ("freq = np.power(base, -(2.0 * i) / r)", "freq = np.power(base, -(1.0 * i) / r)"),
+    "partial rotary exponent uses head dim": ("freq = np.power(base, -(2.0 * i) / r)",
+                                              "freq = np.power(base, -(2.0 * i) / d)"),
+    "partial rotary tail zeroed": ("out = np.array(x, copy=True)\n    out[..., :r]",
+                                   "out = np.zeros_like(x)\n    out[..., :r]"),
+    "position interpolation multiplies": ("freq = freq / float(scaling[\"factor\"])",
+                                          "freq = freq * float(scaling[\"factor\"])"),
+    "ntk exponent dropped": ("base = base * float(scaling[\"factor\"]) ** (r / (r - 2.0))",
+                             "base = base * float(scaling[\"factor\"])"),
+    "yarn temperature dropped": ("return 0.1 * math.log(float(scaling[\"factor\"])) + 1.0", "return 1.0"),
+    "yarn ramp reversed": ("return (1.0 - gamma) * freq / factor + gamma * freq",
+                           "return gamma * freq / factor + (1.0 - gamma) * freq"),
     "head map modulo": ("Q = bf16_to_f64(q_rot[b, j * g:(j + 1) * g]).reshape(g * T, d)",
                         "Q = bf16_to_f64(q_rot[b, j::n_kv]).reshape(g * T, d)"),
     "mask off by one": ("vis = r <= pos", "vis = r < pos"),
@@ -158,7 +168,51 @@ def pin_sink_closed_form(m):
     return ok
 
 
-PINS = [pin_complex_rotation, pin_frequencies, pin_position_offset, pin_torch_cast, pin_sdpa, pin_bruteforce,
+def pin_partial_rotary(m):
+    # rotating 16 of 32 dims equals full RoPE of a 16-dim head; the tail is copied bit for bit
+    rng = np.random.default_rng(41)
+    q, kn, vn = rb(rng, (1, 2, 2, 32)), rb(rng, (1, 1, 2, 32)), rb(rng, (1, 1, 2, 32))
+    kc, vc = rb(rng, (1, 1, 8, 32)), rb(rng, (1, 1, 8, 32))
+    ok = True
+    for layout in ("interleaved", "half"):
+        qr, kr, _ = m.rope_append(q, kn, vn, kc, vc, np.array([3]), 100.0, layout, rotary_dim=16)
+        q2, k2, _ = m.rope_append(q[..., :16].copy(), kn[..., :16].copy(), vn[..., :16].copy(), kc[..., :16].copy(),
+                                  vc[..., :16].copy(), np.array([3]), 100.0, layout)
+        ok &= np.array_equal(qr[..., :16], q2) and np.array_equal(kr[..., :16], k2)
+        ok &= np.array_equal(qr[..., 16:], q[..., 16:]) and np.array_equal(kr[0, :, 3:5, 16:], kn[0, :, :, 16:])
+        x = rng.standard_normal((2, 32))
+        ok &= np.array_equal(m.rope_rotate(x, 7, 100.0, layout, None, 16)[:, 16:], x[:, 16:])
+    return ok
+
+
+def pin_position_interpolation(m):
+    # PI at position p = plain rotation at p / s, written with complex numbers
+    x = np.random.default_rng(43).standard_normal((3, 16))
+    pos = np.array([5.0, 700.0, 3001.0])
+    got = m.rope_rotate(x, pos, 1.0e4, "interleaved", dict(type="linear", factor=4.0))
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * (pos / 4.0)[:, None] * 1.0e4 ** (-np.arange(8) / 8.0))
+    return np.allclose(got[:, 0::2], z.real, atol=1e-10) and np.allclose(got[:, 1::2], z.imag, atol=1e-10)
+
+
+def pin_ntk_lowest_frequency(m):
+    plain = m.rope_frequencies(5.0e5, 64)
+    ntk = m.rope_frequencies(5.0e5, 64, dict(type="ntk", factor=8.0))
+    return ntk[0] == 1.0 and math.isclose(ntk[-1], plain[-1] / 8.0, rel_tol=1e-12)
+
+
+def pin_yarn(m):
+    sc = dict(type="yarn", factor=16.0, beta_slow=1.0, beta_fast=32.0, original_max_pos=4096.0)
+    plain = m.rope_frequencies(1.0e4, 64)
+    f = m.rope_frequencies(1.0e4, 64, sc)
+    turns = 4096.0 * plain / (2 * math.pi)
+    ok = np.array_equal(f[turns > 32], plain[turns > 32]) and np.allclose(f[turns < 1], plain[turns < 1] / 16.0)
+    rng = np.random.default_rng(47)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    dot = m.rope_rotate(q, 900, 1.0e4, "half", sc) @ m.rope_rotate(k, 900, 1.0e4, "half", sc)
+    return ok and math.isclose(dot, (0.1 * math.log(16.0) + 1.0) ** 2 * (q @ k), rel_tol=1e-10)
+
+
+PINS = [pin_partial_rotary, pin_position_interpolation, pin_ntk_lowest_frequency, pin_yarn, pin_complex_rotation, pin_frequencies, pin_position_offset, pin_torch_cast, pin_sdpa, pin_bruteforce,
         pin_window_rows, pin_window_slice, pin_sink_closed_form]
 
 
