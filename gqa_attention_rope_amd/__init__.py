@@ -24,6 +24,9 @@ GQA_ERR_HIP = -6
 GQA_ROPE_INTERLEAVED = 0
 GQA_ROPE_HALF = 1
 
+# context-extension rules (gqa_rope_params.scaling)
+ROPE_SCALING = {None: 0, "llama3": 1, "linear": 2, "ntk": 3, "yarn": 4}
+
 EXPORTED = (
     "gqa_rope_append",
     "gqa_decode_workspace_bytes",
@@ -50,11 +53,13 @@ class GqaRopeParams(ctypes.Structure):
     _fields_ = [
         ("theta", ctypes.c_double),
         ("layout", ctypes.c_int),
-        ("scaled", ctypes.c_int),
+        ("scaling", ctypes.c_int),
         ("factor", ctypes.c_double),
         ("low_freq_factor", ctypes.c_double),
         ("high_freq_factor", ctypes.c_double),
         ("original_max_pos", ctypes.c_double),
+        ("rotary_dim", ctypes.c_int),
+        ("attn_factor", ctypes.c_double),
     ]
 
 
@@ -153,27 +158,45 @@ def _past(past_len, B):
     return past_len.contiguous()
 
 
-def rope_params(theta, layout="interleaved", scaling=None):
+def rope_params(theta, layout="interleaved", scaling=None, rotary_dim=None):
+    """gqa_rope_params from a scaling dict.
+
+    scaling: None, or a dict whose "type" is "llama3" (the default; factor,
+    low_freq_factor, high_freq_factor, original_max_pos), "linear" (factor),
+    "ntk" (factor) or "yarn" (factor, beta_slow, beta_fast, original_max_pos);
+    any of them may carry "attn_factor".  rotary_dim: None for all d dims.
+    """
     p = GqaRopeParams()
     p.theta = float(theta)
     p.layout = {"interleaved": GQA_ROPE_INTERLEAVED, "half": GQA_ROPE_HALF}[layout]
-    p.scaled = 1 if scaling else 0
-    if scaling:
+    kind = None if not scaling else scaling.get("type", "llama3")
+    if kind not in ROPE_SCALING:
+        raise ValueError(f"unknown RoPE scaling {kind!r}")
+    p.scaling = ROPE_SCALING[kind]
+    if kind is not None:
         p.factor = float(scaling["factor"])
+    if kind == "llama3":
         p.low_freq_factor = float(scaling["low_freq_factor"])
         p.high_freq_factor = float(scaling["high_freq_factor"])
         p.original_max_pos = float(scaling["original_max_pos"])
+    elif kind == "yarn":
+        p.low_freq_factor = float(scaling.get("beta_slow", 1.0))
+        p.high_freq_factor = float(scaling.get("beta_fast", 32.0))
+        p.original_max_pos = float(scaling["original_max_pos"])
+    p.attn_factor = float(scaling.get("attn_factor", 0.0) or 0.0) if scaling else 0.0
+    p.rotary_dim = int(rotary_dim or 0)
     return p
 
 
 # ---------------------------------------------------------------- entry points
 
 def gqa_rope_append(q, k_new, v_new, k_cache, v_cache, past_len, max_past_len, theta,
-                    layout="interleaved", scaling=None, q_rot=None, stream=None):
+                    layout="interleaved", scaling=None, q_rot=None, stream=None, rotary_dim=None):
     """Rotate q and k_new at positions past_len[b] + t and append k_rot, v to the cache.
 
     q [B, n_q, T, d], k_new/v_new [B, n_kv, T, d], caches [B, n_kv, S, d] (bf16, device),
-    past_len int32 [B] (device).  Returns q_rot (a new tensor unless given; may be q).
+    past_len int32 [B] (device).  scaling and rotary_dim as in ``rope_params``.  Returns q_rot (a new
+    tensor unless given; may be q).
     """
     import torch
     B, n_q, T, d = q.shape
@@ -187,7 +210,7 @@ def gqa_rope_append(q, k_new, v_new, k_cache, v_cache, past_len, max_past_len, t
     if q_rot is None:
         q_rot = torch.empty_like(q)
     _bf16(q_rot, "q_rot", (B, n_q, T, d))
-    p = rope_params(theta, layout, scaling)
+    p = rope_params(theta, layout, scaling, rotary_dim)
     _check(lib().gqa_rope_append(_ptr(q), _ptr(q_rot), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(past_len), int(max_past_len), B, n_q, n_kv, T, d, S, ctypes.byref(p),
                                  _stream(stream)))

@@ -88,25 +88,56 @@ int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v
         return GQA_ERR_INVALID_ARG;
     if (!(rope->theta > 0.0) || !isfinite(rope->theta)) return GQA_ERR_INVALID_ARG;
     if (rope->layout != GQA_ROPE_INTERLEAVED && rope->layout != GQA_ROPE_HALF) return GQA_ERR_INVALID_ARG;
-    if (rope->scaled != 0 && rope->scaled != 1) return GQA_ERR_INVALID_ARG;
-    if (rope->scaled) {
-        if (!(rope->factor > 0.0) || !(rope->low_freq_factor > 0.0) ||
-            !(rope->high_freq_factor > rope->low_freq_factor) || !(rope->original_max_pos > 0.0) ||
-            !isfinite(rope->factor) || !isfinite(rope->high_freq_factor) || !isfinite(rope->original_max_pos))
-            return GQA_ERR_INVALID_ARG;
+    const int sc = rope->scaling;
+    if (sc < GQA_ROPE_SCALING_NONE || sc > GQA_ROPE_SCALING_YARN) return GQA_ERR_INVALID_ARG;
+    if (sc != GQA_ROPE_SCALING_NONE) {
+        if (!(rope->factor > 0.0) || !isfinite(rope->factor)) return GQA_ERR_INVALID_ARG;
+        if (sc != GQA_ROPE_SCALING_LLAMA3 && !(rope->factor >= 1.0)) return GQA_ERR_INVALID_ARG;
+        if (sc == GQA_ROPE_SCALING_LLAMA3 || sc == GQA_ROPE_SCALING_YARN) {
+            if (!(rope->low_freq_factor > 0.0) || !(rope->high_freq_factor > rope->low_freq_factor) ||
+                !(rope->original_max_pos > 0.0) || !isfinite(rope->high_freq_factor) ||
+                !isfinite(rope->original_max_pos))
+                return GQA_ERR_INVALID_ARG;
+        }
     }
+    if (!(rope->attn_factor >= 0.0) || !isfinite(rope->attn_factor)) return GQA_ERR_INVALID_ARG;
     int st = check_shape(B, n_q, n_kv, T, d, S, max_past_len);
     if (st != GQA_OK) return st;
+    const int rdim = rope->rotary_dim == 0 ? d : rope->rotary_dim;
+    if (rdim < 16 || rdim % 16 || rdim > d) return GQA_ERR_INVALID_ARG;
     st = ensure_device();
     if (st != GQA_OK) return st;
     gqa::RopeDev rd;
-    rd.theta = rope->theta;
     rd.layout = rope->layout;
-    rd.scaled = rope->scaled;
-    rd.factor = rope->scaled ? rope->factor : 1.0;
-    rd.low_freq_factor = rope->scaled ? rope->low_freq_factor : 1.0;
-    rd.high_freq_factor = rope->scaled ? rope->high_freq_factor : 2.0;
-    rd.original_max_pos = rope->scaled ? rope->original_max_pos : 1.0;
+    rd.rotary_dim = rdim;
+    rd.base = rope->theta;
+    rd.factor = 1.0;
+    rd.low_freq_factor = 1.0;
+    rd.high_freq_factor = 2.0;
+    rd.original_max_pos = 1.0;
+    rd.mode = 0;
+    rd.attn = 1.0;
+    switch (sc) {
+        case GQA_ROPE_SCALING_LLAMA3:
+        case GQA_ROPE_SCALING_YARN:
+            rd.mode = 1;
+            rd.factor = rope->factor;
+            rd.low_freq_factor = rope->low_freq_factor;
+            rd.high_freq_factor = rope->high_freq_factor;
+            rd.original_max_pos = rope->original_max_pos;
+            if (sc == GQA_ROPE_SCALING_YARN) rd.attn = 0.1 * log(rope->factor) + 1.0;
+            break;
+        case GQA_ROPE_SCALING_LINEAR:
+            rd.mode = 2;
+            rd.factor = rope->factor;
+            break;
+        case GQA_ROPE_SCALING_NTK:
+            rd.base = rope->theta * pow(rope->factor, (double)rdim / (double)(rdim - 2));
+            break;
+        default:
+            break;
+    }
+    if (rope->attn_factor > 0.0) rd.attn = rope->attn_factor;
     hipError_t e = gqa::launch_rope_append(
         static_cast<const uint16_t*>(q), static_cast<uint16_t*>(q_rot), static_cast<const uint16_t*>(k_new),
         static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),

@@ -9,10 +9,12 @@ namespace gqa {
 
 // RoPE parameters as the kernels see them (validated on the host).
 struct RopeDev {
-    double theta;
+    double base;  // theta, or the NTK-adjusted base
     double factor, low_freq_factor, high_freq_factor, original_max_pos;
-    int layout;  // 0 interleaved pairs (2i, 2i+1); 1 half pairs (i, i + d/2)
-    int scaled;  // Llama-3 frequency-dependent scaling on/off
+    double attn;  // multiplier of the rotated dims
+    int layout;   // 0 interleaved pairs (2i, 2i+1); 1 half pairs (i, i + r/2)
+    int mode;     // 0 plain frequencies; 1 wavelength ramp (Llama-3 / YaRN); 2 divide by factor (PI)
+    int rotary_dim;  // rotated dims r (multiple of 16, <= d)
 };
 
 // Kernel kinds for the timing hooks.

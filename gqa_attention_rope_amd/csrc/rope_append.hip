@@ -9,7 +9,8 @@
 //
 // A token (t, b) is covered by one or more workgroups of 256 threads; each
 // thread owns one item: 8 pairs of one head of q or of the new k (two 16-byte
-// loads, two 16-byte stores), or 16 values of a v row (copied).  Each
+// loads, two 16-byte stores), or 16 values of a v row or of the unrotated
+// tail of a q/k head (partial rotary, [P7] module L7.3; copied).  Each
 // workgroup computes the d/2 angles of the token's position in fp64 and keeps
 // cos/sin in LDS; the item loads are issued before that, since the source rows
 // do not depend on past_len.  All global accesses are 16-byte and contiguous
@@ -21,13 +22,19 @@ namespace gqa {
 
 namespace {
 
-// Pair frequency, optionally with Llama-3 scaling ([KV] "Training details that
-// matter" names the factor and the two cutoffs; the reading of the rule: short
-// wavelengths keep their frequency, long ones are divided by the factor, and
-// the band between blends the two linearly in original_max_pos / wavelength).
-__device__ double pair_frequency(int i, int d, const RopeDev& rp) {
-    double f = pow(rp.theta, -(2.0 * (double)i) / (double)d);
-    if (rp.scaled) {
+// Pair frequency over the r rotated dims, base^(-2i/r), then the context
+// extension rule ([P7] module L7.4 names PI, NTK, YaRN and Llama-3 scaling;
+// [KV] "Training details that matter" names the Llama-3 fields; the pages give
+// no formulas, so each rule is its published definition):
+//   mode 1, the wavelength ramp shared by Llama-3 scaling and YaRN: short
+//     wavelengths keep their frequency, long ones are divided by the factor,
+//     and the band between blends the two linearly in original_max_pos /
+//     wavelength (the turns the pair makes over the original context);
+//   mode 2, position interpolation: every frequency divided by the factor;
+//   NTK-aware scaling only changes the base, which the host has already done.
+__device__ double pair_frequency(int i, int r, const RopeDev& rp) {
+    double f = pow(rp.base, -(2.0 * (double)i) / (double)r);
+    if (rp.mode == 1) {
         const double two_pi = 6.283185307179586476925286766559;
         double wavelength = two_pi / f;
         double long_cut = rp.original_max_pos / rp.low_freq_factor;
@@ -41,6 +48,8 @@ __device__ double pair_frequency(int i, int d, const RopeDev& rp) {
                        (rp.high_freq_factor - rp.low_freq_factor);
             f = (1.0 - s) * f / rp.factor + s * f;
         }
+    } else if (rp.mode == 2) {
+        f = f / rp.factor;
     }
     return f;
 }
@@ -78,17 +87,18 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uin
     const int head = active ? it / ITEMS_PER_HEAD : 0;
     const int c = it % ITEMS_PER_HEAD;
     const bool is_v = head >= n_q + n_kv, is_k = !is_v && head >= n_q;
-    // two 16-byte pieces: 8 (a, b) pairs, or 16 values of v
+    const int R = rp.rotary_dim;          // multiple of 16, <= D (checked on the host)
+    const bool turns = !is_v && 16 * c < R;  // else 16 values copied as they are
+    // two 16-byte pieces: 8 (a, b) pairs, or 16 values copied
     const uint16_t* src;
-    int off0, off1;
-    if (is_v) {
+    if (is_v)
         src = v_new + ((size_t)(b * n_kv + head - n_q - n_kv) * T + t) * D;
-        off0 = 16 * c;
-        off1 = 16 * c + 8;
-    } else {
+    else
         src = is_k ? k_new + ((size_t)(b * n_kv + head - n_q) * T + t) * D : q + ((size_t)(b * n_q + head) * T + t) * D;
-        off0 = rp.layout == 0 ? 16 * c : 8 * c;
-        off1 = rp.layout == 0 ? 16 * c + 8 : HALF + 8 * c;
+    int off0 = 16 * c, off1 = 16 * c + 8;
+    if (turns && rp.layout != 0) {  // half: pair i is dims (i, i + R/2)
+        off0 = 8 * c;
+        off1 = R / 2 + 8 * c;
     }
     uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
     if (active) {
@@ -98,25 +108,27 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uin
 
     if (P < 0 || P > max_past_len) return;  // caller error: write nothing for this sequence
     const int pos = P + t;                  // < max_past_len + T <= S (checked on the host)
-    for (int i = threadIdx.x; i < HALF; i += blockDim.x) {
-        double ang = (double)pos * pair_frequency(i, D, rp);
+    for (int i = threadIdx.x; i < R / 2; i += blockDim.x) {
+        double ang = (double)pos * pair_frequency(i, R, rp);
         double sn, cs;
         sincos(ang, &sn, &cs);
-        s_cos[i] = cs;
-        s_sin[i] = sn;
+        s_cos[i] = rp.attn * cs;  // attention factor (1 unless YaRN or given)
+        s_sin[i] = rp.attn * sn;
     }
     __syncthreads();
     if (!active) return;
 
     uint16_t* dst;
-    if (is_v) {
+    if (is_v)
         dst = v_cache + ((size_t)(b * n_kv + head - n_q - n_kv) * S + pos) * D;
+    else
+        dst = is_k ? k_cache + ((size_t)(b * n_kv + head - n_q) * S + pos) * D
+                   : q_rot + ((size_t)(b * n_q + head) * T + t) * D;
+    if (!turns) {
         *reinterpret_cast<uint4*>(dst + off0) = x0;
         *reinterpret_cast<uint4*>(dst + off1) = x1;
         return;
     }
-    dst = is_k ? k_cache + ((size_t)(b * n_kv + head - n_q) * S + pos) * D
-               : q_rot + ((size_t)(b * n_q + head) * T + t) * D;
     uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     uint32_t o[8];
     if (rp.layout == 0) {

@@ -59,14 +59,40 @@ extern "C" {
 #define GQA_ROPE_INTERLEAVED 0 /* pair i is dims (2i, 2i+1) */
 #define GQA_ROPE_HALF 1        /* pair i is dims (i, i + d/2) */
 
+/* Context-extension rules ([P7] module L7.4 names PI, NTK, YaRN and Llama-3
+ * scaling; [KV] "Training details that matter" names the Llama-3 fields).  The
+ * pages print no formulas; each rule follows its published definition:
+ *   LLAMA3  wavelength lambda = 2 pi / freq: lambda < original_max_pos /
+ *           high_freq_factor keeps freq, lambda > original_max_pos /
+ *           low_freq_factor gives freq / factor, between the two the mix
+ *           (1 - s) freq / factor + s freq, s = (original_max_pos / lambda -
+ *           low_freq_factor) / (high_freq_factor - low_freq_factor).
+ *   LINEAR  position interpolation: every frequency divided by factor.
+ *   NTK     NTK-aware base change: theta becomes theta * factor^(r / (r - 2)).
+ *   YARN    YaRN's ramp in rho = original_max_pos / lambda (the turns a pair
+ *           makes over the original context): the LLAMA3 mix with
+ *           low_freq_factor = alpha (beta_slow, rho below it: freq / factor)
+ *           and high_freq_factor = beta (beta_fast, rho above it: freq), plus
+ *           the attention factor 0.1 ln(factor) + 1 on the rotated dims. */
+#define GQA_ROPE_SCALING_NONE 0
+#define GQA_ROPE_SCALING_LLAMA3 1
+#define GQA_ROPE_SCALING_LINEAR 2
+#define GQA_ROPE_SCALING_NTK 3
+#define GQA_ROPE_SCALING_YARN 4
+
 typedef struct gqa_rope_params {
-    double theta;            /* base: freq_i = theta^(-2i/d)  ([KV] "RoPE has to know where it is") */
+    double theta;            /* base: freq_i = theta^(-2i/r)  ([KV] "RoPE has to know where it is") */
     int layout;              /* GQA_ROPE_INTERLEAVED or GQA_ROPE_HALF ([P7] module L7.3) */
-    int scaled;              /* 0: plain RoPE; 1: Llama-3 frequency-dependent scaling below */
-    double factor;           /* Llama-3 scaling: long wavelengths are divided by this (> 0) */
-    double low_freq_factor;  /* wavelengths above original_max_pos / low_freq_factor: fully scaled */
-    double high_freq_factor; /* wavelengths below original_max_pos / high_freq_factor: unchanged */
-    double original_max_pos; /* context length the base model was trained on (> 0) */
+    int scaling;             /* GQA_ROPE_SCALING_*: NONE ignores the four fields below */
+    double factor;           /* context-extension factor s: >= 1 for LINEAR, NTK, YARN; > 0 for LLAMA3 */
+    double low_freq_factor;  /* LLAMA3 low cutoff / YARN alpha (> 0) */
+    double high_freq_factor; /* LLAMA3 high cutoff / YARN beta (> low_freq_factor) */
+    double original_max_pos; /* context length the base model was trained on (> 0; LLAMA3, YARN) */
+    int rotary_dim;          /* r, rotated dims: 0 = all d; else a multiple of 16 in [16, d] ([P7] L7.3
+                                "partial rotary"): dims r .. d-1 are copied, the half layout pairs
+                                dim i with i + r/2, and the exponent uses r */
+    double attn_factor;      /* multiplier of the rotated dims: 0 = default (YARN 0.1 ln(factor) + 1,
+                                otherwise 1), else > 0 and used as given */
 } gqa_rope_params;
 
 /*
@@ -79,9 +105,12 @@ typedef struct gqa_rope_params {
  * [ATL] cache formula: cache rows p = past_len[b] .. past_len[b]+T-1 receive
  * the rotated keys and the values; no other cache row is touched.
  *
+ * With rotary_dim r < d only the first r dims of each head turn (pair i at
+ * freq_i = theta^(-2i/r)); the other dims are copied.
+ *
  * Precision: frequencies, angles, sin/cos and the rotation are computed in
  * fp64 on the device and each result is rounded once to bf16 (nearest, ties
- * to even).  v rows are copied bit for bit.
+ * to even).  v rows and unrotated dims are copied bit for bit.
  *
  *   q        in   [B, n_q, T, d] bf16
  *   q_rot    out  [B, n_q, T, d] bf16, may equal q (rotated in place)
@@ -90,9 +119,9 @@ typedef struct gqa_rope_params {
  *   k_cache  in/out [B, n_kv, S, d] bf16
  *   v_cache  in/out [B, n_kv, S, d] bf16
  *   past_len in   [B] int32 (device)
- *   rope     in   host pointer; theta > 0, layout valid; when scaled:
- *                 factor > 0, 0 < low_freq_factor < high_freq_factor,
- *                 original_max_pos > 0
+ *   rope     in   host pointer; theta > 0, layout and scaling valid, the
+ *                 scaling fields as stated above, rotary_dim 0 or a multiple
+ *                 of 16 in [16, d], attn_factor >= 0 and finite
  * Errors: INVALID_ARG, GROUP, HEAD_DIM, RANGE (max_past_len + T > S), HIP.
  */
 int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v_new, void* k_cache,

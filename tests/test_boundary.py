@@ -31,9 +31,10 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
-def rope(theta=5.0e5, layout=0, scaled=0, factor=8.0, low=1.0, high=4.0, orig=8192.0):
+def rope(theta=5.0e5, layout=0, scaled=0, factor=8.0, low=1.0, high=4.0, orig=8192.0, rdim=0, attn=0.0):
     p = gq.GqaRopeParams()
-    p.theta, p.layout, p.scaled = theta, layout, scaled
+    p.theta, p.layout, p.scaling = theta, layout, scaled
+    p.rotary_dim, p.attn_factor = rdim, attn
     p.factor, p.low_freq_factor, p.high_freq_factor, p.original_max_pos = factor, low, high, orig
     return p
 
@@ -76,6 +77,13 @@ INV, GRP, HD, RNG, WS, HIP = (gq.GQA_ERR_INVALID_ARG, gq.GQA_ERR_GROUP, gq.GQA_E
     (dict(rope=rope(theta=0.0)), INV), (dict(rope=rope(theta=float("nan"))), INV), (dict(rope=rope(layout=2)), INV),
     (dict(rope=rope(scaled=1, factor=0.0)), INV), (dict(rope=rope(scaled=1, low=4.0, high=1.0)), INV),
     (dict(rope=rope(scaled=1, orig=0.0)), INV),
+    (dict(rope=rope(scaled=5)), INV), (dict(rope=rope(scaled=-1)), INV),
+    (dict(rope=rope(scaled=2, factor=0.5)), INV), (dict(rope=rope(scaled=3, factor=0.9)), INV),
+    (dict(rope=rope(scaled=4, factor=0.5)), INV), (dict(rope=rope(scaled=4, low=32.0, high=1.0)), INV),
+    (dict(rope=rope(scaled=4, orig=-1.0)), INV), (dict(rope=rope(scaled=2, factor=float("inf"))), INV),
+    (dict(rope=rope(rdim=8)), INV), (dict(rope=rope(rdim=24)), INV), (dict(rope=rope(rdim=144)), INV),
+    (dict(d=64, rope=rope(rdim=80)), INV), (dict(rope=rope(rdim=-16)), INV),
+    (dict(rope=rope(attn=-1.0)), INV), (dict(rope=rope(attn=float("nan"))), INV),
 ])
 def test_rope_append_validation(kw, code):
     assert append(**kw) == code
@@ -120,6 +128,11 @@ def test_valid_call_without_device_reports_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a device is present")
     assert append() == HIP
+    # every scaling rule with valid fields, partial rotary, an explicit attention factor
+    for r in (rope(scaled=1), rope(scaled=2, factor=4.0), rope(scaled=3, factor=8.0), rope(scaled=4, high=32.0),
+              rope(rdim=16), rope(rdim=112, layout=1), rope(attn=1.2), rope(scaled=2, factor=1.0, low=0.0)):
+        assert append(rope=r) == HIP
+    assert append(d=64, rope=rope(rdim=64)) == HIP
     assert decode() == HIP
     assert prefill() == HIP
     assert gq.gqa_status_string(HIP)

@@ -114,6 +114,64 @@ def test_rope_append_in_place_q():
     assert max_ulp(synth.bits(qd), q_ref) <= 1
 
 
+LIN4 = dict(type="linear", factor=4.0)
+NTK8 = dict(type="ntk", factor=8.0)
+YARN16 = dict(type="yarn", factor=16.0, beta_slow=1.0, beta_fast=32.0, original_max_pos=4096.0)
+
+VARIANT_CASES = [
+    # B, n_q, n_kv, T, d, S, past, theta, layout, scaling, rotary_dim
+    (2, 8, 2, 3, 128, 300, [0, 290], 1.0e4, "interleaved", None, 64),
+    (2, 8, 2, 3, 128, 300, [5, 200], 1.0e4, "half", None, 32),
+    (2, 6, 3, 2, 64, 100, [10, 90], 1.0e4, "half", None, 16),
+    (2, 6, 3, 2, 64, 100, [10, 90], 1.0e4, "interleaved", None, 48),
+    (2, 16, 2, 1, 128, 8192, [8190, 5000], 5.0e5, "interleaved", LIN4, None),
+    (2, 16, 2, 4, 128, 8192, [8000, 30], 5.0e5, "half", NTK8, None),
+    (1, 8, 2, 5, 64, 8192, [7000], 1.0e4, "interleaved", dict(NTK8, factor=4.0), 32),
+    (2, 16, 2, 4, 128, 8192, [8000, 30], 1.0e4, "interleaved", YARN16, None),
+    (1, 8, 2, 5, 128, 8192, [6000], 1.0e4, "half", dict(YARN16, attn_factor=1.3), 64),
+]
+
+
+@pytest.mark.parametrize("case", VARIANT_CASES,
+                         ids=lambda c: f"d{c[4]}{c[8][0]}{(c[9] or {}).get('type', 'plain')}r{c[10] or c[4]}")
+def test_rope_append_variants(case):
+    B, n_q, n_kv, T, d, S, past, theta, layout, scaling, rdim = case
+    say(f"rope_append variant {case}")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=23 + T + d)
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling, rotary_dim=rdim)
+    kc_d, vc_d = dev(kc), dev(vc)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, past_dev(past), max(past), theta, layout,
+                               scaling, rotary_dim=rdim)
+    torch.cuda.synchronize()
+    q_g, kc_g, vc_g = synth.bits(q_rot), synth.bits(kc_d), synth.bits(vc_d)
+    r = rdim or d
+    assert np.array_equal(vc_g, vc_ref)
+    assert np.array_equal(q_g[..., r:], q[..., r:]), "unrotated dims are copied bit for bit"
+    assert max_ulp(q_g, q_ref) <= 1
+    for b in range(B):
+        rows = slice(past[b], past[b] + T)
+        assert np.array_equal(kc_g[b][:, rows, r:], kn[b][..., r:])
+        assert max_ulp(kc_g[b][:, rows], kc_ref[b][:, rows]) <= 1
+        other = np.ones(S, dtype=bool)
+        other[rows] = False
+        assert np.array_equal(kc_g[b][:, other], kc[b][:, other])
+    say(f"  q_rot bit-exact {np.mean(q_g == q_ref):.6f}")
+
+
+def test_decode_after_yarn_partial_rotary():
+    B, n_q, n_kv, d, S, past = 3, 32, 8, 128, 6000, [5999, 4100, 10]
+    say("decode after YaRN + partial rotary")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=77)
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, 1.0e4, "half", YARN16, rotary_dim=64)
+    ref = attend(q_ref, kc_ref, vc_ref, past, n_kv)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), 1.0e4, "half", YARN16,
+                               rotary_dim=64)
+    out = gq.gqa_decode_attn(q_rot, kc_d, vc_d, pl, max(past))
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, "decode after YaRN + partial rotary")
+
+
 # ---------------------------------------------------------------- decode
 
 DECODE_CASES = [
