@@ -33,14 +33,14 @@
 //    one of them has nothing to do its buffer descriptor has a zero range, so
 //    the hardware drops it.  With a path-independent count, every wait for a
 //    stage drains exactly that stage and never the younger prefetches.
-//  * Waves split the tile by (head group, row group).  For q.k, lane
-//    (r = lane/8, e = lane%8) owns 16-byte pieces e and e+8 of a row: a
-//    v_dot2_f32_bf16 chain over those pieces, then a DPP reduction over the 8
-//    lanes of the row.  Online softmax keeps a running max and sum per head
-//    (wave reductions by DPP / lane shuffles).  The weights go through a small
-//    per-wave LDS buffer, and for the weighted value sum every lane owns d/64
-//    output dims of all the wave's heads, so the accumulator is a few
-//    registers.
+//  * Waves split the tile by (head group, row group).  q.k runs on MFMA
+//    (v_mfma_f32_16x16x32_bf16): 16 K rows from an XOR-swizzled LDS tile are
+//    the A operand, the segment's rotated q rows (held in registers) the B
+//    operand, so each 16-row block gives every head's scores at once.  Online
+//    softmax keeps a running max and sum per head (lane shuffles).  The
+//    weights go through a small per-wave LDS buffer, and for the weighted
+//    value sum every lane owns d/64 output dims of all the wave's heads, so
+//    the accumulator is a few registers.
 //  * A second kernel merges the records of each (sequence, head) in a fixed
 //    order: M = max m, l = sum l e^(m-M), o = sum o e^(m-M) / l, and clears
 //    the ticket counter for the next call.  Results are bitwise reproducible
