@@ -107,7 +107,8 @@ def kernel_avg(gq, fn, steps, kind):
         fn()
     torch.cuda.synchronize()
     gq.gqa_profile_enable(False)
-    out = {k: gq.gqa_profile_read(k) for k in ("rope_append", "decode_partial", "decode_combine", "prefill")}
+    out = {k: gq.gqa_profile_read(k) for k in ("rope_append", "decode_partial", "decode_combine", "prefill",
+                                               "decode_step")}
     gq.gqa_profile_reset()
     ms, n = out[kind]
     return ms / max(n, 1), out
@@ -168,6 +169,60 @@ def prefill_workload(gq, synth, dev):
     pairs = sum(sum(int(p) + t + 1 for t in range(T)) for p in past)
     flops = 2 * 2 * n_q * d * pairs
     return step, flops
+
+
+def small_batch_workload(gq, synth, name, dev):
+    """One decode step of a small workload two ways: rope_append + decode_attn, and the single-launch step."""
+    import torch
+    w = synth.WORKLOADS[name]
+    B, n_q, n_kv, d, S = w["B"], w["n_q"], w["n_kv"], w["d"], w["S"]
+    past = synth.past_lengths(B, w["past"], w["seed"])
+    kc = synth.normal_bf16((B, n_kv, S, d), w["seed"] + 3, dev)
+    vc = synth.normal_bf16((B, n_kv, S, d), w["seed"] + 4, dev)
+    q = synth.normal_bf16((B, n_q, 1, d), w["seed"], dev)
+    kn = synth.normal_bf16((B, n_kv, 1, d), w["seed"] + 1, dev)
+    vn = synth.normal_bf16((B, n_kv, 1, d), w["seed"] + 2, dev)
+    pl = torch.as_tensor(past, device=dev)
+    maxp = int(past.max())
+    q_rot, out3, out1 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws3 = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=dev)
+    ws1 = torch.zeros(gq.gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=dev)
+
+    def three():
+        gq.gqa_rope_append(q, kn, vn, kc, vc, pl, maxp, w["theta"], "interleaved", w["scaling"], q_rot=q_rot)
+        gq.gqa_decode_attn(q_rot, kc, vc, pl, maxp, out=out3, workspace=ws3)
+
+    def one():
+        gq.gqa_decode_step(q, kn, vn, kc, vc, pl, maxp, w["theta"], "interleaved", w["scaling"], out=out1,
+                           workspace=ws1)
+
+    return three, one, kv_bytes(past, n_kv, d), B
+
+
+def graph_us(fn, per_graph=20, replays=20):
+    """Device time per call of fn, from a HIP graph of per_graph calls replayed back to back (no host gaps)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (replays * per_graph)
 
 
 def cpu_baseline(info, kc, vc, q, kn, vn):
@@ -293,6 +348,14 @@ def main():
             "tokens_per_s": round(info5["B"] / (ms5 * 1e-3), 1)}
         del s5, t5
         torch.cuda.empty_cache()
+        small = {}
+        for name in ("tiny_decode_g3", "llama8b_layer_decode"):
+            three, one, kvb, Bs = small_batch_workload(gq, synth, name, dev)
+            t3, t1 = graph_us(three), graph_us(one)
+            small[name] = {"rope_append_plus_decode_us": round(t3, 2), "single_launch_step_us": round(t1, 2),
+                           "speedup": round(t3 / t1, 2), "kv_bytes": kvb,
+                           "single_launch_tokens_per_s": round(Bs / (t1 * 1e-6), 1)}
+        extra["small_batch_decode"] = dict(small, timing="HIP graph of 20 steps replayed 20 times, per step")
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(info, *tensors)

@@ -34,6 +34,8 @@ EXPORTED = (
     "gqa_decode_attn_ex",
     "gqa_prefill_attn",
     "gqa_prefill_attn_ex",
+    "gqa_decode_step_workspace_bytes",
+    "gqa_decode_step",
     "gqa_status_string",
     "gqa_profile_enable",
     "gqa_profile_read",
@@ -42,7 +44,7 @@ EXPORTED = (
     "gqa_set_decode_schedule",
 )
 
-KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3}
+KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3, "decode_step": 4}
 
 
 class GqaAttnOpts(ctypes.Structure):
@@ -97,6 +99,11 @@ def lib():
     L.gqa_prefill_attn_ex.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
                                       ctypes.POINTER(GqaAttnOpts), vp]
     L.gqa_prefill_attn_ex.restype = i32
+    L.gqa_decode_step_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.gqa_decode_step_workspace_bytes.restype = ctypes.c_size_t
+    L.gqa_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, i32, i32, i32, i32, i32,
+                                  ctypes.POINTER(GqaRopeParams), f32, ctypes.POINTER(GqaAttnOpts), vp]
+    L.gqa_decode_step.restype = i32
     L.gqa_status_string.argtypes = [i32]
     L.gqa_status_string.restype = ctypes.c_char_p
     L.gqa_profile_enable.argtypes = [i32]
@@ -286,6 +293,45 @@ def gqa_prefill_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, 
     _check(lib().gqa_prefill_attn_ex(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
                                      _ptr(out), B, n_q, n_kv, T, d, S, float(scale),
                                      ctypes.byref(opts) if opts else None, _stream(stream)))
+    return out
+
+
+def gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S):
+    return int(lib().gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S))
+
+
+def gqa_decode_step(q, k_new, v_new, k_cache, v_cache, past_len, max_past_len, theta, layout="interleaved",
+                    scaling=None, rotary_dim=None, out=None, q_rot=None, workspace=None, scale=0.0, stream=None,
+                    window=0, n_sink=0, sink_logits=None):
+    """One decode step in a single launch: rotate q and k_new at past_len, append k_rot and v_new to the
+    caches, attend over rows 0..past_len (or the window and sinks).  Returns out [B, n_q, 1, d] bf16;
+    q_rot, when given, receives the rotated q.  A workspace must start zeroed (the default one is)."""
+    import torch
+    B, n_q, T, d = q.shape
+    if T != 1:
+        raise ValueError("decode takes exactly one new token per sequence")
+    n_kv, S = k_cache.shape[1], k_cache.shape[2]
+    _bf16(q, "q")
+    _bf16(k_new, "k_new", (B, n_kv, 1, d))
+    _bf16(v_new, "v_new", (B, n_kv, 1, d))
+    _bf16(k_cache, "k_cache", (B, n_kv, S, d))
+    _bf16(v_cache, "v_cache", (B, n_kv, S, d))
+    past_len = _past(past_len, B)
+    if out is None:
+        out = torch.empty_like(q)
+    _bf16(out, "out", (B, n_q, 1, d))
+    if q_rot is not None:
+        _bf16(q_rot, "q_rot", (B, n_q, 1, d))
+    need = gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    p = rope_params(theta, layout, scaling, rotary_dim)
+    opts, _keep = _opts(window, n_sink, sink_logits, n_q, q.device)
+    _check(lib().gqa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(past_len),
+                                 int(max_past_len), _ptr(out), _ptr(q_rot) if q_rot is not None else None,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), B, n_q, n_kv, d, S,
+                                 ctypes.byref(p), float(scale), ctypes.byref(opts) if opts else None,
+                                 _stream(stream)))
     return out
 
 

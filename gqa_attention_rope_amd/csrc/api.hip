@@ -28,6 +28,8 @@ int check_shape(int B, int n_q, int n_kv, int T, int d, int S, int max_past_len)
     if (n_q % n_kv) return GQA_ERR_GROUP;
     if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
     if (max_past_len < 0 || (long long)max_past_len + T > (long long)S) return GQA_ERR_RANGE;
+    // one KV head's cache slab is addressed with 32-bit byte offsets
+    if ((long long)S * d * 2 > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
     return GQA_OK;
 }
 
@@ -77,15 +79,8 @@ void prof_end(int kind, hipStream_t st) {
 
 }  // namespace gqa
 
-extern "C" {
-
-int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v_new, void* k_cache,
-                    void* v_cache, const int32_t* past_len, int max_past_len, int B, int n_q, int n_kv, int T,
-                    int d, int S, const gqa_rope_params* rope, void* stream) {
-    if (!q || !q_rot || !k_new || !v_new || !k_cache || !v_cache || !past_len || !rope) return GQA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(q_rot) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-        !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(past_len) & 3u))
-        return GQA_ERR_INVALID_ARG;
+// Validate RoPE parameters for head size d and fill the device-side form.
+static int make_rope(const gqa_rope_params* rope, int d, gqa::RopeDev& rd) {
     if (!(rope->theta > 0.0) || !isfinite(rope->theta)) return GQA_ERR_INVALID_ARG;
     if (rope->layout != GQA_ROPE_INTERLEAVED && rope->layout != GQA_ROPE_HALF) return GQA_ERR_INVALID_ARG;
     const int sc = rope->scaling;
@@ -101,13 +96,8 @@ int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v
         }
     }
     if (!(rope->attn_factor >= 0.0) || !isfinite(rope->attn_factor)) return GQA_ERR_INVALID_ARG;
-    int st = check_shape(B, n_q, n_kv, T, d, S, max_past_len);
-    if (st != GQA_OK) return st;
     const int rdim = rope->rotary_dim == 0 ? d : rope->rotary_dim;
     if (rdim < 16 || rdim % 16 || rdim > d) return GQA_ERR_INVALID_ARG;
-    st = ensure_device();
-    if (st != GQA_OK) return st;
-    gqa::RopeDev rd;
     rd.layout = rope->layout;
     rd.rotary_dim = rdim;
     rd.base = rope->theta;
@@ -138,6 +128,26 @@ int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v
             break;
     }
     if (rope->attn_factor > 0.0) rd.attn = rope->attn_factor;
+    return GQA_OK;
+}
+
+extern "C" {
+
+
+int gqa_rope_append(const void* q, void* q_rot, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, const int32_t* past_len, int max_past_len, int B, int n_q, int n_kv, int T,
+                    int d, int S, const gqa_rope_params* rope, void* stream) {
+    if (!q || !q_rot || !k_new || !v_new || !k_cache || !v_cache || !past_len || !rope) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(q_rot) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(past_len) & 3u))
+        return GQA_ERR_INVALID_ARG;
+    int st = check_shape(B, n_q, n_kv, T, d, S, max_past_len);
+    if (st != GQA_OK) return st;
+    gqa::RopeDev rd;
+    st = make_rope(rope, d, rd);
+    if (st != GQA_OK) return st;
+    st = ensure_device();
+    if (st != GQA_OK) return st;
     hipError_t e = gqa::launch_rope_append(
         static_cast<const uint16_t*>(q), static_cast<uint16_t*>(q_rot), static_cast<const uint16_t*>(k_new),
         static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
@@ -179,6 +189,43 @@ int gqa_decode_attn(const void* q_rot, const void* k_cache, const void* v_cache,
                     int d, int S, float scale, void* stream) {
     return gqa_decode_attn_ex(q_rot, k_cache, v_cache, past_len, max_past_len, out, workspace, workspace_bytes, B,
                               n_q, n_kv, d, S, scale, nullptr, stream);
+}
+
+size_t gqa_decode_step_workspace_bytes(int B, int n_q, int n_kv, int d, int S) {
+    if (check_shape(B, n_q, n_kv, 1, d, S, 0) != GQA_OK) return 0;
+    if (n_q / n_kv > GQA_DECODE_STEP_MAX_GROUP || B > 65535 || n_kv > 65535) return 0;
+    return gqa::decode_step_workspace_bytes(B, n_q, n_kv, d);
+}
+
+int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* past_len, int max_past_len, void* out, void* q_rot, void* workspace,
+                    size_t workspace_bytes, int B, int n_q, int n_kv, int d, int S, const gqa_rope_params* rope,
+                    float scale, const gqa_attn_opts* opts, void* stream) {
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !past_len || !out || !workspace || !rope)
+        return GQA_ERR_INVALID_ARG;
+    const gqa_attn_opts o = opts ? *opts : gqa_attn_opts{0, 0, nullptr};
+    if (o.window < 0 || o.n_sink < 0 || (o.sink_logits && (reinterpret_cast<uintptr_t>(o.sink_logits) & 3u)))
+        return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(out) || (q_rot && !aligned16(q_rot)) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(past_len) & 3u))
+        return GQA_ERR_INVALID_ARG;
+    if (!(scale == scale) || isinf(scale)) return GQA_ERR_INVALID_ARG;
+    int st = check_shape(B, n_q, n_kv, 1, d, S, max_past_len);
+    if (st != GQA_OK) return st;
+    if (n_q / n_kv > GQA_DECODE_STEP_MAX_GROUP || B > 65535 || n_kv > 65535) return GQA_ERR_INVALID_ARG;
+    gqa::RopeDev rd;
+    st = make_rope(rope, d, rd);
+    if (st != GQA_OK) return st;
+    if (workspace_bytes < gqa::decode_step_workspace_bytes(B, n_q, n_kv, d)) return GQA_ERR_WORKSPACE;
+    st = ensure_device();
+    if (st != GQA_OK) return st;
+    hipError_t e = gqa::launch_decode_step(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), past_len, max_past_len,
+        static_cast<uint16_t*>(out), static_cast<uint16_t*>(q_rot), workspace, B, n_q, n_kv, d, S, rd,
+        resolve_scale(scale, d), o.window, o.n_sink, o.sink_logits, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : hip_status(e);
 }
 
 int gqa_prefill_attn_ex(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,

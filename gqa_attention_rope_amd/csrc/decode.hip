@@ -47,6 +47,7 @@
 //    for a given launch shape.
 #include <float.h>
 
+#include "attn_window.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -77,35 +78,6 @@ struct Cfg {
     static constexpr int LOADS = 2 * TILE * PPR / THREADS;  // 16-byte loads per thread per tile
 };
 
-// Visible rows of the new query of a sequence with L = past_len + 1 cached
-// rows: all of them, or, under a sliding window of W rows, the sink rows
-// 0 .. n_sink-1 and the window rows w0 .. L-1 with w0 = L - W.  The tiles of
-// the segment are the nst sink tiles 0 .. nst-1 followed by the window tiles
-// at0, at0+1, .. (absolute 64-row tile indices); when the two ranges meet
-// (or there is no window) the tiles are simply 0 .. ceil(L/64)-1 and w0 = 0.
-struct Geo {
-    int nt;   // tiles of the segment
-    int nst;  // leading tiles (sinks, or all of them when contiguous)
-    int at0;  // absolute index of the first window tile
-    int w0;   // first visible window row (0 when every row is visible)
-};
-__device__ __forceinline__ Geo geo_of(int L, int window, int n_sink) {
-    Geo g;
-    const int all = (L + TILE - 1) / TILE;
-    if (window <= 0 || L - window <= n_sink) {
-        g.nt = all;
-        g.nst = all;
-        g.at0 = all;
-        g.w0 = 0;
-    } else {
-        g.w0 = L - window;
-        g.nst = (n_sink + TILE - 1) / TILE;
-        const int a0 = g.w0 / TILE;
-        g.at0 = a0 > g.nst ? a0 : g.nst;
-        g.nt = g.nst + all - g.at0;
-    }
-    return g;
-}
 __device__ __forceinline__ int rows_clamped(const int32_t* past_len, int b, int pmax) {
     int P = past_len[b];
     P = P < 0 ? 0 : (P > pmax ? pmax : P);
@@ -861,6 +833,18 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
     if (G <= 0) {
         const int bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
         G = cu_count * (d == 128 ? v.occ128(bs) : v.occ64(bs));
+    }
+    // never more workgroups than tiles: a small problem would otherwise have
+    // most workgroups queue on the ticket counter with nothing to do
+    {
+        long long per_seg = (max_past_len + 1 + TILE - 1) / TILE;
+        if (window > 0) {
+            const long long wt = (n_sink + TILE - 1) / TILE + (window + TILE - 1) / TILE + 1;
+            if (wt < per_seg) per_seg = wt;
+        }
+        const long long bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
+        const long long tiles = bs * n_kv * p.nhc * per_seg;
+        if (G > tiles) G = (int)tiles;
     }
     if (G > DECODE_MAX_WG) G = DECODE_MAX_WG;
     if (G < 1) G = 1;

@@ -18,7 +18,14 @@ struct RopeDev {
 };
 
 // Kernel kinds for the timing hooks.
-enum KernelKind { K_ROPE_APPEND = 0, K_DECODE_PARTIAL = 1, K_DECODE_COMBINE = 2, K_PREFILL = 3, K_KINDS = 4 };
+enum KernelKind {
+    K_ROPE_APPEND = 0,
+    K_DECODE_PARTIAL = 1,
+    K_DECODE_COMBINE = 2,
+    K_PREFILL = 3,
+    K_DECODE_STEP = 4,
+    K_KINDS = 5
+};
 
 // Timing hooks (no-ops unless enabled through gqa_profile_enable).
 void prof_begin(int kind, hipStream_t st);
@@ -65,5 +72,17 @@ hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const 
                           const int32_t* past_len, int max_past_len, uint16_t* out, int B, int n_q, int n_kv, int T,
                           int d, int S, float scale, int window, int n_sink, const float* sink_logits,
                           hipStream_t st);
+
+// ---- single-launch decode step (rope + append + attention + merge) ------------
+// Most splits of one (sequence, KV head) segment; sizes the workspace.
+constexpr int DECODE_STEP_MAX_SPLITS = 64;
+// Splits a launch uses: about two workgroups per CU over all segments, at most
+// one per tile of the longest context and at most DECODE_STEP_MAX_SPLITS.
+int decode_step_splits(int B, int n_kv, int max_past_len, int window, int n_sink);
+size_t decode_step_workspace_bytes(int B, int n_q, int n_kv, int d);
+hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
+                              uint16_t* v_cache, const int32_t* past_len, int max_past_len, uint16_t* out,
+                              uint16_t* q_rot, void* ws, int B, int n_q, int n_kv, int d, int S, const RopeDev& rope,
+                              float scale, int window, int n_sink, const float* sink_logits, hipStream_t st);
 
 }  // namespace gqa

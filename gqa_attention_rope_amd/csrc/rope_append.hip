@@ -17,49 +17,11 @@
 // along d.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "rope_math.hpp"
 
 namespace gqa {
 
 namespace {
-
-// Pair frequency over the r rotated dims, base^(-2i/r), then the context
-// extension rule ([P7] module L7.4 names PI, NTK, YaRN and Llama-3 scaling;
-// [KV] "Training details that matter" names the Llama-3 fields; the pages give
-// no formulas, so each rule is its published definition):
-//   mode 1, the wavelength ramp shared by Llama-3 scaling and YaRN: short
-//     wavelengths keep their frequency, long ones are divided by the factor,
-//     and the band between blends the two linearly in original_max_pos /
-//     wavelength (the turns the pair makes over the original context);
-//   mode 2, position interpolation: every frequency divided by the factor;
-//   NTK-aware scaling only changes the base, which the host has already done.
-__device__ double pair_frequency(int i, int r, const RopeDev& rp) {
-    double f = pow(rp.base, -(2.0 * (double)i) / (double)r);
-    if (rp.mode == 1) {
-        const double two_pi = 6.283185307179586476925286766559;
-        double wavelength = two_pi / f;
-        double long_cut = rp.original_max_pos / rp.low_freq_factor;
-        double short_cut = rp.original_max_pos / rp.high_freq_factor;
-        if (wavelength < short_cut) {
-            // unchanged
-        } else if (wavelength > long_cut) {
-            f = f / rp.factor;
-        } else {
-            double s = (rp.original_max_pos / wavelength - rp.low_freq_factor) /
-                       (rp.high_freq_factor - rp.low_freq_factor);
-            f = (1.0 - s) * f / rp.factor + s * f;
-        }
-    } else if (rp.mode == 2) {
-        f = f / rp.factor;
-    }
-    return f;
-}
-
-// (a, b) -> (a cos - b sin, a sin + b cos), fp64, each output rounded once to bf16.
-__device__ __forceinline__ void turn(float a, float b, double c, double s, uint32_t& ra, uint32_t& rb) {
-    double da = (double)a, db = (double)b;
-    ra = f64_to_bf16_rne(da * c - db * s);
-    rb = f64_to_bf16_rne(da * s + db * c);
-}
 
 // One workgroup covers up to 256 items of one token (t, b); an item is 8 pairs
 // of one head (two 16-byte pieces), of q, of the new k, or of v (copied).  The
@@ -129,29 +91,9 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uin
         *reinterpret_cast<uint4*>(dst + off1) = x1;
         return;
     }
-    uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     uint32_t o[8];
-    if (rp.layout == 0) {
-        // interleaved: word m holds pair 8c + m as (lo, hi) = (a, b)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int i = 8 * c + m;
-            uint32_t ra, rb;
-            turn(bf_lo(w[m]), bf_hi(w[m]), s_cos[i], s_sin[i], ra, rb);
-            o[m] = ra | (rb << 16);
-        }
-    } else {
-        // half: value m of piece 0 pairs with value m of piece 1 (pair 8c + m)
-#pragma unroll
-        for (int m = 0; m < 8; m += 2) {
-            const int i = 8 * c + m;
-            uint32_t ra0, rb0, ra1, rb1;
-            turn(bf_lo(w[m / 2]), bf_lo(w[4 + m / 2]), s_cos[i], s_sin[i], ra0, rb0);
-            turn(bf_hi(w[m / 2]), bf_hi(w[4 + m / 2]), s_cos[i + 1], s_sin[i + 1], ra1, rb1);
-            o[m / 2] = ra0 | (ra1 << 16);
-            o[4 + m / 2] = rb0 | (rb1 << 16);
-        }
-    }
+    rotate_item(w, c, rp.layout, s_cos, s_sin, o);
     *reinterpret_cast<uint4*>(dst + off0) = make_uint4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<uint4*>(dst + off1) = make_uint4(o[4], o[5], o[6], o[7]);
 }

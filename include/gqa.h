@@ -20,7 +20,9 @@
  *        past_len       [B]  int32, rows already cached for each sequence
  *   - n_q = g * n_kv; query head h reads KV head floor(h / g) ([REP] formula;
  *     [EP18] "Our six heads, three ways").  No copy of a KV head is made.
- *   - d is 64 or 128 (the kernels are built for these two head sizes).
+ *   - d is 64 or 128 (the kernels are built for these two head sizes), and
+ *     S * d * 2 < 2^31 (one KV head's cache slab is addressed with 32-bit
+ *     byte offsets; INVALID_ARG otherwise).
  *   - past_len lives in device memory so that calls can be captured and
  *     replayed; max_past_len is the host-side upper bound the caller vouches
  *     for (past_len[b] <= max_past_len for every b).  Every launch is sized
@@ -225,6 +227,44 @@ int gqa_prefill_attn_ex(const void* q_rot, const void* k_cache, const void* v_ca
                         int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
                         const gqa_attn_opts* opts, void* stream);
 
+/*
+ * gqa_decode_step -- one decode step in a single launch, for small batches:
+ * gqa_rope_append (T = 1) followed by gqa_decode_attn, same results.
+ *
+ * [KV] "RoPE has to know where it is" and "The cache itself is
+ * concatenation"; [ATL] "Llama 3 8B - KV cache", cache formula and the
+ * Transformer.forward excerpt (write row past_len, then attend over rows
+ * 0 .. past_len); [REP] head map h -> floor(h / g).  The new token's q and k
+ * are rotated at position past_len[b] (fp64, one rounding to bf16), k_rot
+ * and v_new are written to cache row past_len[b], and the new query attends
+ * to rows 0 .. past_len[b] (under opts: the window, sinks and learned sink
+ * logits of gqa_attn_opts).  The new row enters the attention from the
+ * kernel's registers, so the result never depends on when the append lands.
+ * The splits of each (sequence, KV head) are merged by the last one to
+ * finish, in split order: bitwise reproducible for a given shape.
+ *
+ *   q, k_new, v_new in [B, n_q | n_kv, 1, d] bf16 (q and k unrotated)
+ *   k_cache, v_cache in/out [B, n_kv, S, d] bf16; row past_len[b] is written
+ *   out      out [B, n_q, 1, d] bf16
+ *   q_rot    out [B, n_q, 1, d] bf16, or NULL (not written)
+ *   rope     host pointer, as for gqa_rope_append
+ *   scale    <= 0 selects 1/sqrt(d)
+ *   workspace  device memory of gqa_decode_step_workspace_bytes(); its first
+ *            bytes hold one counter per (sequence, KV head), which must be zero
+ *            before the first call (allocate it zero-filled); every call leaves
+ *            them zero.  Calls that share a workspace must be stream-ordered,
+ *            and it must not be shared with gqa_decode_attn.
+ * n_q / n_kv must be at most GQA_DECODE_STEP_MAX_GROUP; B and n_kv at most
+ * 65535.  Errors: INVALID_ARG, GROUP, HEAD_DIM, RANGE (max_past_len + 1 > S),
+ * WORKSPACE, HIP.
+ */
+#define GQA_DECODE_STEP_MAX_GROUP 64
+size_t gqa_decode_step_workspace_bytes(int B, int n_q, int n_kv, int d, int S);
+int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* past_len, int max_past_len, void* out, void* q_rot, void* workspace,
+                    size_t workspace_bytes, int B, int n_q, int n_kv, int d, int S, const gqa_rope_params* rope,
+                    float scale, const gqa_attn_opts* opts, void* stream);
+
 /* Human-readable text for a status code; for GQA_ERR_HIP it includes the
  * last HIP error message recorded by this thread.  Never NULL. */
 const char* gqa_status_string(int status);
@@ -235,7 +275,7 @@ const char* gqa_status_string(int status);
  * the launch stream; gqa_profile_read synchronises those events and returns
  * the summed device time and launch count of one kernel kind.
  *   kind: 0 rope_append, 1 decode split-K partials, 2 decode combine,
- *         3 prefill.
+ *         3 prefill, 4 single-launch decode step.
  * Not thread-safe; for single-threaded benchmark drivers.
  */
 int gqa_profile_enable(int on);

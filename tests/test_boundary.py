@@ -223,3 +223,51 @@ def test_python_binding_validates_attention_options():
         a.update(bad)
         with pytest.raises(ValueError):
             gq._opts(a["window"], a["n_sink"], a["sink_logits"], 8, "cpu")
+
+
+def step(o=None, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, pl=FAKE, maxp=10, out=FAKE, q_rot=None, ws=FAKE,
+             wsb=1 << 40, B=2, n_q=8, n_kv=2, d=128, S=64, rope=rope(), scale=0.0)
+    a.update(kw)
+    r = a["rope"]
+    return gq.lib().gqa_decode_step(P(a["q"]), P(a["kn"]), P(a["vn"]), P(a["kc"]), P(a["vc"]), P(a["pl"]), a["maxp"],
+                                    P(a["out"]), P(a["q_rot"]), P(a["ws"]), a["wsb"], a["B"], a["n_q"], a["n_kv"],
+                                    a["d"], a["S"], None if r is None else ctypes.byref(r), a["scale"],
+                                    None if o is None else ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INV), (dict(kn=0), INV), (dict(ws=0), INV), (dict(rope=None), INV), (dict(out=FAKE + 8), INV),
+    (dict(q_rot=FAKE + 4), INV), (dict(pl=FAKE + 1), INV), (dict(B=0), INV), (dict(n_q=8, n_kv=3), GRP),
+    (dict(d=96), HD), (dict(maxp=64, S=64), RNG), (dict(maxp=-1), RNG), (dict(wsb=0), WS),
+    (dict(n_q=130, n_kv=2), INV), (dict(scale=float("nan")), INV), (dict(rope=rope(rdim=24)), INV),
+    (dict(rope=rope(scaled=4, factor=0.5)), INV), (dict(S=1 << 23, maxp=10), INV),
+])
+def test_decode_step_validation(kw, code):
+    assert step(**kw) == code
+
+
+def test_decode_step_options_and_workspace_query():
+    assert step(opts(window=-1)) == INV
+    assert step(opts(n_sink=-1)) == INV
+    assert step(opts(window=4, sink=FAKE + 2)) == INV
+    L = gq.lib()
+    n = L.gqa_decode_step_workspace_bytes(2, 8, 2, 128, 64)
+    assert n > 0 and n % 16 == 0
+    assert step(wsb=n - 1) == WS
+    assert L.gqa_decode_step_workspace_bytes(2, 8, 3, 128, 64) == 0
+    assert L.gqa_decode_step_workspace_bytes(1, 130, 2, 128, 64) == 0
+    assert L.gqa_decode_step_workspace_bytes(2, 128, 2, 128, 64) > 0  # g = 64, the largest group
+    import torch
+    if not torch.cuda.is_available():
+        assert step() == HIP
+        assert step(opts(window=16, n_sink=4, sink=FAKE), q_rot=FAKE) == HIP
+
+
+def test_every_entry_point_checks_the_slab_size():
+    """S * d * 2 must stay below 2^31: the kernels address one KV head's slab with 32-bit offsets."""
+    big = dict(S=1 << 23, maxp=10)
+    assert decode(**big) == INV
+    assert prefill(**big) == INV
+    assert append(**big) == INV
+    assert step(**big) == INV

@@ -463,3 +463,131 @@ def test_prefill_window_and_sinks(case):
                               sink_logits=sk)
     torch.cuda.synchronize()
     check_out(synth.bits(out), ref, f"prefill window {W} sinks {NS}")
+
+
+# ---------------------------------------------------------------- single-launch decode step
+
+STEP_CASES = [
+    # B, n_q, n_kv, d, S, past, theta, layout, scaling, rotary_dim, window, n_sink, learned sinks
+    (1, 6, 2, 64, 256, [255], 1.0e4, "interleaved", None, None, 0, 0, False),       # tiny 6/2-head window
+    (1, 32, 8, 128, 8192, [1000], 5.0e5, "interleaved", None, None, 0, 0, False),   # one Llama-3.1-8B layer
+    (4, 32, 8, 128, 300, [0, 63, 64, 299], 5.0e5, "interleaved", None, None, 0, 0, False),  # L = 1, tile edges
+    (3, 64, 8, 128, 600, [511, 300, 599], 5.0e5, "interleaved", SCALED, None, 0, 0, False),  # g = 8, scaled
+    (2, 8, 8, 128, 200, [150, 9], 5.0e5, "half", None, None, 0, 0, False),           # g = 1
+    (2, 6, 1, 64, 300, [299, 77], 1.0e4, "interleaved", None, None, 0, 0, False),    # g = 6 (MQA)
+    (2, 32, 1, 128, 400, [399, 5], 5.0e5, "interleaved", None, None, 0, 0, False),   # g = 32 (MQA)
+    (1, 64, 1, 128, 200, [150], 5.0e5, "half", None, None, 0, 0, True),              # g = 64
+    (3, 32, 8, 128, 3000, [2999, 10, 1500], 5.0e5, "interleaved", None, None, 256, 4, True),  # window + sinks
+    (2, 32, 8, 128, 5000, [4999, 100], 1.0e4, "half", YARN16, 64, 0, 0, False),     # YaRN, partial rotary
+    (2, 24, 2, 64, 2000, [1999, 1000], 1.0e4, "half", NTK8, None, 100, 70, False),  # g = 12, window meets sinks
+]
+
+
+def run_step(case, seed, ws=None):
+    B, n_q, n_kv, d, S, past, theta, layout, scaling, rdim, W, NS, learned = case
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed)
+    for b in range(B):  # the row being appended: never read before it is written
+        kc[b, :, past[b]] = synth.NAN_BF16
+        vc[b, :, past[b]] = synth.NAN_BF16
+    sinks = np.random.default_rng(seed).standard_normal(n_q).astype(np.float32) if learned else None
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling, rotary_dim=rdim)
+    ref = attend(q_ref, kc_ref, vc_ref, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    q_rot = torch.empty(B, n_q, 1, d, dtype=torch.bfloat16, device=DEV)
+    out = gq.gqa_decode_step(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling, rdim,
+                             q_rot=q_rot, workspace=ws, window=W, n_sink=NS,
+                             sink_logits=torch.from_numpy(sinks).to(DEV) if learned else None)
+    torch.cuda.synchronize()
+    return out, ref, (q_rot, q_ref, kc_d, kc_ref, vc_d, vc_ref, kc)
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}d{c[3]}W{c[10]}"
+                         f"{(c[8] or {}).get('type', 'plain') if c[8] else ''}")
+def test_decode_step_parity(case):
+    say(f"decode_step {case}")
+    B, S, past = case[0], case[4], case[5]
+    out, ref, (q_rot, q_ref, kc_d, kc_ref, vc_d, vc_ref, kc_in) = run_step(case, seed=900 + case[1] + case[3])
+    check_out(synth.bits(out), ref, "decode_step")
+    assert max_ulp(synth.bits(q_rot), q_ref) <= 1
+    kc_g, vc_g = synth.bits(kc_d), synth.bits(vc_d)
+    assert np.array_equal(vc_g, vc_ref), "value row appended bit for bit, nothing else touched"
+    for b in range(B):
+        other = np.ones(S, dtype=bool)
+        other[past[b]] = False
+        assert np.array_equal(kc_g[b][:, other], kc_in[b][:, other])
+        assert max_ulp(kc_g[b][:, past[b]], kc_ref[b][:, past[b]]) <= 1
+
+
+def test_decode_step_repeat_calls_and_workspace_reuse():
+    """Two calls on one workspace give identical bits, and the per-segment counters end at zero."""
+    case = STEP_CASES[1]
+    B, n_q, n_kv, d, S = case[0], case[1], case[2], case[3], case[4]
+    ws = torch.zeros(gq.gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    out1, ref, _ = run_step(case, seed=5, ws=ws)
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    out2, _, _ = run_step(case, seed=5, ws=ws)
+    assert torch.equal(out1, out2)
+    check_out(synth.bits(out2), ref, "decode_step second call")
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+
+
+def test_decode_step_matches_three_call_path():
+    case = (2, 32, 8, 128, 3000, [2999, 1234], 5.0e5, "interleaved", SCALED)
+    B, n_q, n_kv, d, S, past, theta, layout, scaling = case
+    say("decode_step vs rope_append + decode_attn")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=31)
+    kc1, vc1, kc2, vc2, pl = dev(kc), dev(vc), dev(kc), dev(vc), past_dev(past)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc1, vc1, pl, max(past), theta, layout, scaling)
+    o3 = gq.gqa_decode_attn(q_rot, kc1, vc1, pl, max(past))
+    q_rot2 = torch.empty_like(q_rot)
+    o1 = gq.gqa_decode_step(dev(q), dev(kn), dev(vn), kc2, vc2, pl, max(past), theta, layout, scaling, q_rot=q_rot2)
+    torch.cuda.synchronize()
+    assert torch.equal(q_rot, q_rot2)
+    # bit patterns (the caches hold NaN poison beyond the appended row)
+    assert np.array_equal(synth.bits(kc1), synth.bits(kc2)) and np.array_equal(synth.bits(vc1), synth.bits(vc2))
+    diff = (o1.float() - o3.float()).abs().max().item()
+    assert diff <= 2 ** -7, diff  # two orders of the same fp32 sums, each rounded once to bf16
+
+
+def test_graph_replays_match_eager():
+    """Both decode paths captured in a HIP graph: every replay equals the eager result bit for bit."""
+    B, n_q, n_kv, d, S, past, theta = 2, 32, 8, 128, 2000, [1999, 700], 5.0e5
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=61)
+    qd, knd, vnd, pl = dev(q), dev(kn), dev(vn), past_dev(past)
+    kc1, vc1, kc2, vc2 = dev(kc), dev(vc), dev(kc), dev(vc)
+    q_rot, o3, o1 = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    ws3 = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    ws1 = torch.zeros(gq.gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+
+    def three():
+        gq.gqa_rope_append(qd, knd, vnd, kc1, vc1, pl, max(past), theta, q_rot=q_rot)
+        gq.gqa_decode_attn(q_rot, kc1, vc1, pl, max(past), out=o3, workspace=ws3)
+
+    def one():
+        gq.gqa_decode_step(qd, knd, vnd, kc2, vc2, pl, max(past), theta, out=o1, workspace=ws1)
+
+    three()
+    one()
+    torch.cuda.synchronize()
+    e3, e1 = o3.clone(), o1.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        three()
+        one()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        three()
+        one()
+    for rep in range(3):
+        o3.zero_()
+        o1.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o3, e3) and torch.equal(o1, e1), f"replay {rep}"
+        three()  # eager work between replays
+        torch.cuda.synchronize()
+    assert int(ws1[:256].view(torch.int32).abs().sum()) == 0 and int(ws3[:256].view(torch.int32).abs().sum()) == 0
