@@ -131,6 +131,11 @@ __device__ __forceinline__ long long owner_of(long long tau, long long T, long l
 struct Cursor {
     int b, sj, tt, nt, L;  // tt: index among the segment's nt tiles
     int nst, at0, w0;      // the sequence's tile geometry (see geo_of)
+    // kept up to date by the cursor so that issuing a tile needs no division:
+    int hc;                // head chunk of the segment (sj % nhc)
+    int seg;               // global segment index b * segs_per_b + sj
+    int qoff;              // element offset of the segment's query rows in q_rot
+    long long kvoff;       // element offset of the segment's K (and V) slab
 };
 
 // Byte offset in the LDS tile of 16-byte piece c of row R (rows of D bf16).
@@ -236,11 +241,24 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         c.nst = uni(gg.nst);
         c.at0 = uni(gg.at0);
         c.w0 = uni(gg.w0);
+        const int j = c.sj / nhc;
+        c.hc = c.sj - j * nhc;
+        c.seg = c.b * segs_per_b + c.sj;
+        c.qoff = (c.b * n_q + j * g + c.hc * C::GC) * D;
+        c.kvoff = (long long)(c.b * n_kv + j) * S * D;
         return c;
     };
+    // next tile; on a segment change the q rows move by one head chunk and the
+    // K/V slab by one KV head whenever the head chunks of a KV head are done
     auto advance = [&] __attribute__((always_inline)) (Cursor& c) {
         if (++c.tt < c.nt) return;
         c.tt = 0;
+        ++c.seg;
+        c.qoff += C::GC * D;
+        if (++c.hc == nhc) {
+            c.hc = 0;
+            c.kvoff += (long long)S * D;
+        }
         if (++c.sj < segs_per_b) return;
         c.sj = 0;
         if (++c.b < B) {
@@ -257,6 +275,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     // most one ticket in flight or in hand
     Cursor ld;
     ld.b = 0; ld.sj = 0; ld.tt = 0; ld.nt = 1; ld.L = 1; ld.nst = 1; ld.at0 = 1; ld.w0 = 0;
+    ld.hc = 0; ld.seg = 0; ld.qoff = 0; ld.kvoff = 0;
     const int tau_w = (int)share_begin(w, sc.Ts, G);
     int ld_left = (int)share_begin(w + 1, sc.Ts, G) - tau_w;
     int ld_rid = w;
@@ -300,7 +319,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         stg.tt = uni(at);
         stg.L = uni(ld.L);
         stg.w0 = uni(ld.w0);
-        stg.slot = uni(ld_rid + ld.b * segs_per_b + ld.sj);
+        stg.slot = uni(ld_rid + ld.seg);
         stg.flags = uni((tile ? K_TILE : ((no_more && !pending) ? K_END : K_BUBBLE)) |
                         ((ld_left == 1 || ld.tt + 1 == ld.nt) ? F_PIECE_END : 0) | (grab ? F_GRABBED : 0));
         if (grab) pending = true;
@@ -311,7 +330,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
             __builtin_amdgcn_make_buffer_rsrc((void*)ticket_ctr, (short)0, uni(grab ? 4 : 0), RSRC_FLAGS);
         tkbuf = __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, rt, tid == 0 ? 0 : OOB, 0, 0);
         // K/V rows of the tile; thread tid loads bytes tid*16 + x*4096 of each
-        const size_t seg_off = (size_t)uni(ld.b * n_kv + ld.sj / nhc) * S * D;
+        const long long seg_off = ld.kvoff;
         const int valid_bytes = uni(tile ? ld.L * ROWB : 0);
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg_off), (short)0, valid_bytes, RSRC_FLAGS);
@@ -324,8 +343,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
             buf[HALF + x] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + x * THREADS * 16, 0);
         }
         {
-            const int j = ld.sj / nhc, hc = ld.sj % nhc;
-            const uint16_t* qseg = q_rot + (size_t)uni(ld.b * n_q + j * g + hc * C::GC) * D;
+            const uint16_t* qseg = q_rot + ld.qoff;
             const __amdgpu_buffer_rsrc_t rq =
                 __builtin_amdgcn_make_buffer_rsrc((void*)qseg, (short)0, uni(tile ? QPIECES * 16 : 0), RSRC_FLAGS);
             qbuf = __builtin_amdgcn_raw_buffer_load_b128(rq, tid < QPIECES ? tid * 16 : OOB, 0, 0);

@@ -47,7 +47,7 @@ constexpr int DECODE_MAX_WG = 2048;
 // tiles handed out by a ticket counter (at most DECODE_MAX_CHUNKS chunks; the
 // chunk grows when a launch would need more).
 constexpr int DECODE_DEFAULT_STATIC_PM = 700;
-constexpr int DECODE_DEFAULT_CHUNK = 3;
+constexpr int DECODE_DEFAULT_CHUNK = 4;
 constexpr int DECODE_MAX_CHUNKS = 8192;
 
 struct DecodePlan {
