@@ -108,7 +108,7 @@ def kernel_avg(gq, fn, steps, kind):
     torch.cuda.synchronize()
     gq.gqa_profile_enable(False)
     out = {k: gq.gqa_profile_read(k) for k in ("rope_append", "decode_partial", "decode_combine", "prefill",
-                                               "decode_step")}
+                                               "decode_step", "decode_wide")}
     gq.gqa_profile_reset()
     ms, n = out[kind]
     return ms / max(n, 1), out
@@ -223,6 +223,27 @@ def graph_us(fn, per_graph=20, replays=20):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / (replays * per_graph)
+
+
+def wide_group_workload(gq, synth, dev, B, n_q, n_kv, seed):
+    """Decode attention for a wide query group (g = n_q / n_kv >= 16), ragged contexts U[2048, 8191]."""
+    import torch
+    d, S = 128, 8192
+    past = synth.past_lengths(B, ("uniform", 2048, 8191), seed)
+    kc = torch.empty((B, n_kv, S, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    synth.fill_normal_bf16_(kc, seed * 1000)
+    synth.fill_normal_bf16_(vc, seed * 1000 + 1)
+    q = synth.normal_bf16((B, n_q, 1, d), seed + 11, dev)
+    pl = torch.as_tensor(past, device=dev)
+    maxp = int(past.max())
+    out = torch.empty_like(q)
+    ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=dev)
+
+    def call():
+        gq.gqa_decode_attn(q, kc, vc, pl, maxp, out=out, workspace=ws)
+
+    return call, kv_bytes(past, n_kv, d)
 
 
 def cpu_baseline(info, kc, vc, q, kn, vn):
@@ -356,6 +377,20 @@ def main():
                            "speedup": round(t3 / t1, 2), "kv_bytes": kvb,
                            "single_launch_tokens_per_s": round(Bs / (t1 * 1e-6), 1)}
         extra["small_batch_decode"] = dict(small, timing="HIP graph of 20 steps replayed 20 times, per step")
+        wide = {}
+        for (Bw, nqw, nkvw, seed) in ((16, 64, 1, 1006), (32, 32, 2, 1007)):
+            call, kvb = wide_group_workload(gq, synth, dev, Bw, nqw, nkvw, seed)
+            t_wide = graph_us(call)
+            gq.gqa_set_decode_wide_min_group(65)  # the split-K path on the same call
+            t_split = graph_us(call)
+            gq.gqa_set_decode_wide_min_group(0)
+            wide[f"B{Bw}_{nqw}q_{nkvw}kv_g{nqw // nkvw}"] = {
+                "wide_kernel_us": round(t_wide, 2), "kv_gbs": round(kvb / (t_wide * 1e-6) / 1e9, 1),
+                "split_k_us": round(t_split, 2), "speedup": round(t_split / t_wide, 2), "kv_bytes": kvb}
+            del call
+            torch.cuda.empty_cache()
+        extra["wide_group_decode"] = dict(wide, context="past_len U[2048,8191] seeded, d 128, S 8192",
+                                          timing="HIP graph of 20 calls replayed 20 times, per call")
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(info, *tensors)

@@ -42,9 +42,11 @@ EXPORTED = (
     "gqa_profile_reset",
     "gqa_set_decode_workgroups",
     "gqa_set_decode_schedule",
+    "gqa_set_decode_wide_min_group",
 )
 
-KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3, "decode_step": 4}
+KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3, "decode_step": 4,
+                "decode_wide": 5}
 
 
 class GqaAttnOpts(ctypes.Structure):
@@ -114,6 +116,8 @@ def lib():
     L.gqa_profile_reset.restype = i32
     L.gqa_set_decode_workgroups.argtypes = [i32]
     L.gqa_set_decode_workgroups.restype = i32
+    L.gqa_set_decode_wide_min_group.argtypes = [i32]
+    L.gqa_set_decode_wide_min_group.restype = i32
     L.gqa_set_decode_schedule.argtypes = [i32, i32]
     L.gqa_set_decode_schedule.restype = i32
     _lib = L
@@ -359,3 +363,8 @@ def gqa_set_decode_workgroups(n):
 def gqa_set_decode_schedule(static_permille=-1, chunk_tiles=0):
     """Static fraction (per mille) and dynamic chunk size of the decode split; (-1, 0) = defaults."""
     _check(lib().gqa_set_decode_schedule(int(static_permille), int(chunk_tiles)))
+
+
+def gqa_set_decode_wide_min_group(g=0):
+    """Smallest group size the wide-group decode kernel takes; 0 = default, > 64 = off."""
+    return int(lib().gqa_set_decode_wide_min_group(int(g)))

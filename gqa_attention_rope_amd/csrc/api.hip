@@ -312,6 +312,11 @@ int gqa_set_decode_workgroups(int n) {
     return g_decode_wg;
 }
 
+int gqa_set_decode_wide_min_group(int g) {
+    gqa::set_decode_wide_min_group(g);
+    return gqa::decode_wide_min_group();
+}
+
 int gqa_set_decode_schedule(int static_permille, int chunk_tiles) {
     if (static_permille < 0 && chunk_tiles <= 0) {
         gqa::set_decode_schedule(gqa::DECODE_DEFAULT_STATIC_PM, gqa::DECODE_DEFAULT_CHUNK);

@@ -61,7 +61,7 @@ constexpr int WAVES = THREADS / 64;
 constexpr float LOG2E = 1.4426950408889634f;
 // The workspace starts with a 256-byte scheduling header (the ticket counter
 // at offset 0); the records follow.
-constexpr int HDR_FLOATS = 64;
+constexpr int HDR_FLOATS = DECODE_WS_HEADER_FLOATS;
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;  // raw buffer, 32-bit dwords
 constexpr int OOB = 0x7ffffff0;               // a buffer offset past any range: the access is dropped
 
@@ -828,13 +828,30 @@ size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d) {
     const size_t segs = (size_t)bs * n_kv * p.nhc;
     // static pieces: segment + workgroup < segs + G; chunk pieces: segs + G + chunk + segment
     const size_t slots = 2 * segs + DECODE_MAX_WG + DECODE_MAX_CHUNKS;
-    return (HDR_FLOATS + slots * p.slot_floats) * sizeof(float);
+    size_t need = (HDR_FLOATS + slots * p.slot_floats) * sizeof(float);
+    // the same workspace serves the wide-group kernel when it takes the shape
+    const int g = n_q / n_kv;
+    if (g <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS) {
+        const size_t wide = HDR_FLOATS * sizeof(float) + decode_wide_record_bytes(B, n_q, n_kv, d);
+        if (wide > need) need = wide;
+    }
+    return need;
 }
+
+namespace {
+int g_wide_min = DECODE_WIDE_MIN_G;
+}  // namespace
+
+void set_decode_wide_min_group(int g) { g_wide_min = g > 0 ? g : DECODE_WIDE_MIN_G; }
+int decode_wide_min_group() { return g_wide_min; }
 
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
                          int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
                          int wg_override, hipStream_t st) {
+    if (n_q / n_kv >= g_wide_min && n_q / n_kv <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS)
+        return launch_decode_wide(q_rot, k_cache, v_cache, past_len, max_past_len, out, ws, B, n_q, n_kv, d, S, scale,
+                                  window, n_sink, sink_logits, wg_override, st);
     const DecodePlan p = decode_plan(n_q, n_kv, d);
     const Variant& v = pick_variant(n_q / n_kv);
 

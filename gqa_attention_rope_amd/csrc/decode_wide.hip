@@ -1,0 +1,372 @@
+// Decode attention for wide query groups (g > 16 query heads per KV head, up
+// to multi-query attention with g = n_q): both products on MFMA, each K/V row
+// read once for all g heads.
+//
+// What is computed is the same as the split-K decode path ([KV] "Llama 3.1 8B
+// KV cache", "The cache itself is concatenation"; [REP] "Llama 3.1 8B - Repeat
+// heads" formula: query head h reads KV head floor(h / g); [EP18]
+// "Grouped-query attention: a smaller KV cache", where n_kv = 1 is MQA): the
+// new query of each head attends to cache rows 0 .. past_len[b] (or its
+// window and sinks).
+//
+// Why a separate kernel: with g query heads per K/V row the work per byte is
+// g times that of one head.  The split-K kernel keeps at most 16 heads per
+// segment (its weighted value sum runs on VALU) and streams the rows again
+// for every further 16; here a workgroup keeps all g heads and both q.k and
+// the weighted value sum are dense [g x 64] products on the matrix cores.
+//
+// How:
+//  * Grid (split, KV head j, sequence b), 4 waves.  A segment's tiles (64 rows;
+//    sink and window tiles only, under a window) are cut into nsplit
+//    contiguous ranges.  Wave w owns head block hb = w % HB (16 heads) and row
+//    group w / HB of each tile (RG = 4 / HB groups of 64 / RG rows).
+//  * A tile's K rows go to LDS row-major with an XOR swizzle (the MFMA A
+//    operand reads 16 rows of one 16-byte piece), V rows transposed (dim-major
+//    with a padded stride, so that the B operand's 4-row runs of one dim are
+//    8-byte reads on distinct banks).  One register stage prefetches the next
+//    tile while the current one is computed.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A: 16 K rows x 32 dims; B: the
+//    wave's 16 rotated q rows, held in registers).  Lane l then holds rows
+//    4(l/16)+i of each 16-row block for head l%16: exactly the A operand of
+//    O += P V when the 32 rows of a K-step are taken in that order, so P never
+//    leaves the registers.  P enters as a bf16 high part plus a bf16
+//    remainder (two MFMAs, about 16 significant bits); V's B operand follows
+//    the same row order (two 8-byte reads per lane).
+//  * Online softmax per head (two lane shuffles per reduction); the output
+//    rescale fetches each head's factor from the lanes that own it.
+//  * Each (split, row group) writes one (max, sum, unnormalised output)
+//    record per head.  The split count keeps every segment's records (all
+//    heads of all splits) within 1024, so that for large g the records stay
+//    small next to the K/V rows they summarise.  A second kernel merges the
+//    records of each (sequence, query head) in a fixed order with one wave per
+//    head: reproducible for a given shape.
+#include <float.h>
+
+#include "attn_window.hpp"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gqa {
+
+namespace {
+
+constexpr int WD_THREADS = 256;
+constexpr int WD_TILE = 64;
+constexpr float WD_LOG2E = 1.4426950408889634f;
+constexpr uint32_t WD_RSRC = 0x00020000u;  // raw buffer, 32-bit dwords
+constexpr int WD_VS = 68;                  // transposed V tile: elements per dim (64 rows + pad)
+
+__device__ __forceinline__ float wd_wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ float wd_wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// D head size; HB blocks of 16 heads (g <= 16 HB), HB in {2, 4}
+template <int D, int HB>
+__global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
+    const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ past_len, int pmax, float* __restrict__ recs, int n_q, int n_kv, int S, int nsplit,
+    float scale_log2, int window, int n_sink) {
+    constexpr int PPR = D / 8;                       // 16-byte pieces per row
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = WD_TILE * ROWB;            // bytes of one tensor's tile
+    constexpr int HALF = TILEB / (16 * WD_THREADS);  // 16-byte loads per thread per tensor
+    constexpr int RG = 4 / HB;                       // row groups
+    constexpr int ROWS_W = WD_TILE / RG;             // rows of a tile per wave (32 or 64)
+    constexpr int KB = ROWS_W / 16;                  // 16-row blocks per wave
+    constexpr int KS = D / 32;                       // MFMA k-steps over the head dim
+    constexpr int DB = D / 16;                       // 16-dim blocks of the output
+    constexpr int REC = D + 4;
+    constexpr int NREC = RG;                         // records per split and head
+
+    __shared__ __align__(16) unsigned char s_k[TILEB];
+    __shared__ __align__(16) uint16_t s_vt[D * WD_VS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int hb = wave % HB, rg = wave / HB;
+    const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int g = n_q / n_kv;
+    int P = past_len[b];
+    P = P < 0 ? 0 : (P > pmax ? pmax : P);
+    const int L = P + 1;
+    const Geo geo = geo_of(L, window, n_sink);
+    const int t0 = (int)((long long)sp * geo.nt / nsplit);
+    const int t1 = (int)((long long)(sp + 1) * geo.nt / nsplit);
+    auto abs_tile = [&](int i) { return i < geo.nst ? i : geo.at0 + (i - geo.nst); };
+
+    // K/V rows 0 .. L-1 of the segment (the hardware range check zero-fills the rest)
+    const size_t seg = (size_t)(b * n_kv + j) * S * D;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg), (short)0, L * ROWB, WD_RSRC);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg), (short)0, L * ROWB, WD_RSRC);
+    u32x4_t kb[HALF], vb[HALF];
+    auto load_tile = [&](int i) {
+        const int base = abs_tile(i) * TILEB + tid * 16;
+#pragma unroll
+        for (int x = 0; x < HALF; ++x) {
+            kb[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + x * WD_THREADS * 16, 0, 0);
+            vb[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + x * WD_THREADS * 16, 0, 0);
+        }
+    };
+    if (t0 < t1) load_tile(t0);
+
+    // B operand of the scores: 8 dims of head 16 hb + l16 per k-step (zero beyond g)
+    const int hq = 16 * hb + l16;
+    bf16x8_t qop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (hq < g) v = *reinterpret_cast<const u32x4_t*>(q_rot + (size_t)(b * n_q + j * g + hq) * D + 32 * ks + 8 * lq);
+        qop[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;  // head l16 of the block (l_run: this lane's share)
+    f32x4_t oacc[DB];                      // O[head 4 lq + i][dim 16 db + l16]
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int i = t0; i < t1; ++i) {
+        const int at = abs_tile(i);
+        __syncthreads();  // the previous tile is consumed
+#pragma unroll
+        for (int x = 0; x < HALF; ++x) {
+            const int byte = tid * 16 + x * WD_THREADS * 16;
+            const int row = byte / ROWB, pc = (byte % ROWB) / 16;
+            *reinterpret_cast<u32x4_t*>(s_k + row * ROWB + 16 * (pc ^ (row & (PPR - 1)))) = kb[x];
+            const uint32_t w4[4] = {vb[x][0], vb[x][1], vb[x][2], vb[x][3]};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s_vt[(8 * pc + 2 * e) * WD_VS + row] = (uint16_t)(w4[e] & 0xffffu);
+                s_vt[(8 * pc + 2 * e + 1) * WD_VS + row] = (uint16_t)(w4[e] >> 16);
+            }
+        }
+        if (i + 1 < t1) load_tile(i + 1);
+        __syncthreads();
+
+        // scores of this wave's rows for its 16 heads
+        f32x4_t sacc[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            sacc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int r = rg * ROWS_W + 16 * k + l16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4_t kv =
+                    *reinterpret_cast<const u32x4_t*>(s_k + r * ROWB + 16 * ((4 * ks + lq) ^ (r & (PPR - 1))));
+                sacc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qop[ks], sacc[k],
+                                                                   0, 0, 0);
+            }
+        }
+        // online softmax for head l16 over rows rg*ROWS_W + 16k + 4lq + e
+        float tm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = at * WD_TILE + rg * ROWS_W + 16 * k + 4 * lq + e;
+                const bool vis = row < L && (row >= geo.w0 || row < n_sink);
+                sacc[k][e] = vis ? sacc[k][e] * scale_log2 : -INFINITY;
+                tm = fmaxf(tm, sacc[k][e]);
+            }
+        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        const float mn = fmaxf(m_run, tm);
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run - mn);
+        m_run = mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sacc[k][e] = fast_exp2(sacc[k][e] - mref);
+                ps += sacc[k][e];
+            }
+        l_run = l_run * alpha + ps;
+        // rescale the output rows: lane holds heads 4 lq + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = __shfl(alpha, 4 * lq + e, 64);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db][e] *= a;
+        }
+        // O += P V, 32 rows per k-step: k index 8 lq + e <-> row 16 (2 kk) + 4 lq + e (e < 4),
+        // row 16 (2 kk + 1) + 4 lq + e - 4 (e >= 4), the order the score registers already have
+#pragma unroll
+        for (int kk = 0; kk < KB / 2; ++kk) {
+            const f32x4_t p0 = sacc[2 * kk], p1 = sacc[2 * kk + 1];
+            const uint32_t h0 = cvt_pk_bf16(p0[0], p0[1]), h1 = cvt_pk_bf16(p0[2], p0[3]);
+            const uint32_t h2 = cvt_pk_bf16(p1[0], p1[1]), h3 = cvt_pk_bf16(p1[2], p1[3]);
+            const u32x4_t hi = {h0, h1, h2, h3};
+            const u32x4_t lo = {cvt_pk_bf16(p0[0] - bf_lo(h0), p0[1] - bf_hi(h0)),
+                                cvt_pk_bf16(p0[2] - bf_lo(h1), p0[3] - bf_hi(h1)),
+                                cvt_pk_bf16(p1[0] - bf_lo(h2), p1[1] - bf_hi(h2)),
+                                cvt_pk_bf16(p1[2] - bf_lo(h3), p1[3] - bf_hi(h3))};
+            const int r0 = rg * ROWS_W + 32 * kk + 4 * lq;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const uint16_t* vcol = s_vt + (16 * db + l16) * WD_VS;
+                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vcol + r0);
+                const u32x2_t c = *reinterpret_cast<const u32x2_t*>(vcol + r0 + 16);
+                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], c[0], c[1]});
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), bop, oacc[db], 0,
+                                                                    0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), bop, oacc[db], 0,
+                                                                    0, 0);
+            }
+        }
+    }
+
+    // ---- records of this (split, row group): (m, l, pad, pad, o[D]) per head
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    const size_t segi = (size_t)b * n_kv + j;
+    float* rbase = recs + ((segi * nsplit + sp) * NREC + rg) * g * REC;
+    if (lq == 0 && hq < g) *reinterpret_cast<float2*>(rbase + (size_t)hq * REC) = make_float2(m_run, l_run);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int h = 16 * hb + 4 * lq + e;
+        if (h < g) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) rbase[(size_t)h * REC + 4 + 16 * db + l16] = oacc[db][e];
+        }
+    }
+}
+
+// Merge the records of one (sequence, query head) in order: M = max m,
+// out = sum o e^(m - M) / (sum l e^(m - M) [+ e^(sink - M)]).  One wave; lane r
+// holds record r's (m, l), and the outputs are read eight records at a time.
+template <int D>
+__global__ __launch_bounds__(64) void decode_wide_combine_kernel(const float* __restrict__ recs,
+                                                                 uint16_t* __restrict__ out, int n_q, int n_kv,
+                                                                 int nrec, const float* __restrict__ sink_logits) {
+    constexpr int REC = D + 4, DPL = D / 64;
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int g = n_q / n_kv, j = h / g, hl = h % g;
+    // record r of head hl: recs + ((segment * nrec + r) * g + hl) * REC, records ordered by (split, row group)
+    const float* r0p = recs + ((size_t)(b * n_kv + j) * nrec * g + hl) * REC;
+    const size_t stride = (size_t)g * REC;
+    float m_l = -INFINITY, l_l = 0.f;
+    if (lane < nrec) {  // nrec <= 64
+        const float2 ml = *reinterpret_cast<const float2*>(r0p + lane * stride);
+        m_l = ml.x;
+        l_l = ml.y;
+    }
+    const float sk = sink_logits ? sink_logits[h] * WD_LOG2E : -INFINITY;
+    const float M = fmaxf(wd_wave_max(m_l), sk);
+    const float w_l = m_l == -INFINITY ? 0.f : fast_exp2(m_l - M);  // 0 for lanes >= nrec
+    const float lsum = wd_wave_sum(w_l * l_l) + (sk == -INFINITY ? 0.f : fast_exp2(sk - M));
+    float acc[DPL];
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
+    for (int q0 = 0; q0 < nrec; q0 += 8) {
+        float ov[8][DPL];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = q0 + u < nrec ? q0 + u : 0;
+            const float* rr = r0p + r * stride + 4 + DPL * lane;
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) ov[u][x] = rr[x];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            // q0 + u <= 63 (q0 is a multiple of 8 below nrec <= 64); lanes >= nrec hold 0
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), q0 + u));
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) acc[x] += w * ov[u][x];
+        }
+    }
+    const float inv = 1.f / lsum;
+    uint16_t* dst = out + (size_t)(b * n_q + h) * D;
+    if (DPL == 2)
+        *reinterpret_cast<uint32_t*>(dst + 2 * lane) = cvt_pk_bf16(acc[0] * inv, acc[DPL - 1] * inv);
+    else
+        dst[lane] = (uint16_t)(cvt_pk_bf16(acc[0] * inv, 0.f) & 0xffffu);
+}
+
+using wide_fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int, float*, int, int, int,
+                         int, float, int, int);
+
+}  // namespace
+
+// records per segment (all heads of all splits) stay within this many, so that
+// the records written and merged remain small next to the K/V rows they cover
+constexpr int WD_MAX_SEG_RECORDS = 1024;
+
+int decode_wide_splits(int nb, int n_kv, int g, int max_past_len, int window, int n_sink, int wg_override) {
+    static int cu_count = 0;
+    if (cu_count == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cu_count = 256;
+    }
+    long long tiles = (max_past_len + 1 + 63) / 64;
+    if (window > 0) {
+        const long long wt = (n_sink + 63) / 64 + window / 64 + 2;
+        if (wt < tiles) tiles = wt;
+    }
+    const long long segs = (long long)nb * n_kv;
+    const long long target = wg_override > 0 ? wg_override : 2LL * cu_count;
+    long long n = (target + segs - 1) / segs;
+    const int rg = g <= 32 ? 2 : 1;
+    const long long cap = WD_MAX_SEG_RECORDS / (rg * g);
+    if (n > cap) n = cap;
+    if (n > tiles) n = tiles;
+    if (n > DECODE_WIDE_MAX_SPLITS) n = DECODE_WIDE_MAX_SPLITS;
+    return n < 1 ? 1 : (int)n;
+}
+
+size_t decode_wide_record_bytes(int B, int n_q, int n_kv, int d) {
+    int nb = DECODE_WIDE_MAX_SEGS / n_kv;
+    if (nb > B) nb = B;
+    // at most WD_MAX_SEG_RECORDS records per segment
+    return (size_t)nb * n_kv * WD_MAX_SEG_RECORDS * (d + 4) * sizeof(float);
+}
+
+hipError_t launch_decode_wide(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
+                              const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
+                              int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
+                              int wg_override, hipStream_t st) {
+    const int g = n_q / n_kv;
+    const int rg = g <= 32 ? 2 : 1;
+    float* recs = ws + DECODE_WS_HEADER_FLOATS;
+    wide_fn fn;
+    if (d == 128)
+        fn = g <= 32 ? decode_wide_kernel<128, 2> : decode_wide_kernel<128, 4>;
+    else
+        fn = g <= 32 ? decode_wide_kernel<64, 2> : decode_wide_kernel<64, 4>;
+    const int per = DECODE_WIDE_MAX_SEGS / n_kv;  // sequences per launch (bounds the record space)
+    for (int b0 = 0; b0 < B; b0 += per) {
+        const int nb = (B - b0) < per ? (B - b0) : per;
+        const int nsplit = decode_wide_splits(nb, n_kv, g, max_past_len, window, n_sink, wg_override);
+        prof_begin(K_DECODE_WIDE, st);
+        hipLaunchKernelGGL(fn, dim3(nsplit, n_kv, nb), dim3(WD_THREADS), 0, st, q_rot + (size_t)b0 * n_q * d,
+                           k_cache + (size_t)b0 * n_kv * S * d, v_cache + (size_t)b0 * n_kv * S * d, past_len + b0,
+                           max_past_len, recs, n_q, n_kv, S, nsplit, scale * WD_LOG2E, window, n_sink);
+        prof_end(K_DECODE_WIDE, st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        prof_begin(K_DECODE_COMBINE, st);
+        if (d == 128)
+            hipLaunchKernelGGL(decode_wide_combine_kernel<128>, dim3(n_q, nb), dim3(64), 0, st, recs,
+                               out + (size_t)b0 * n_q * d, n_q, n_kv, nsplit * rg, sink_logits);
+        else
+            hipLaunchKernelGGL(decode_wide_combine_kernel<64>, dim3(n_q, nb), dim3(64), 0, st, recs,
+                               out + (size_t)b0 * n_q * d, n_q, n_kv, nsplit * rg, sink_logits);
+        prof_end(K_DECODE_COMBINE, st);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace gqa

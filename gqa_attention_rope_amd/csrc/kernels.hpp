@@ -24,7 +24,8 @@ enum KernelKind {
     K_DECODE_COMBINE = 2,
     K_PREFILL = 3,
     K_DECODE_STEP = 4,
-    K_KINDS = 5
+    K_DECODE_WIDE = 5,
+    K_KINDS = 6
 };
 
 // Timing hooks (no-ops unless enabled through gqa_profile_enable).
@@ -84,5 +85,23 @@ hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const ui
                               uint16_t* v_cache, const int32_t* past_len, int max_past_len, uint16_t* out,
                               uint16_t* q_rot, void* ws, int B, int n_q, int n_kv, int d, int S, const RopeDev& rope,
                               float scale, int window, int n_sink, const float* sink_logits, hipStream_t st);
+
+// ---- decode for wide query groups (g > 16: both products on MFMA) -------------
+// The decode workspace starts with a header of this many floats (256 bytes)
+// that holds the split-K ticket counter; records follow it.
+constexpr int DECODE_WS_HEADER_FLOATS = 64;
+constexpr int DECODE_WIDE_MIN_G = 16;       // used from this group size on
+constexpr int DECODE_WIDE_MAX_G = 64;
+constexpr int DECODE_WIDE_MAX_SEGS = 64;    // segments per launch (bounds the record space)
+constexpr int DECODE_WIDE_MAX_SPLITS = 32;  // splits per segment
+int decode_wide_splits(int nb, int n_kv, int g, int max_past_len, int window, int n_sink, int wg_override);
+size_t decode_wide_record_bytes(int B, int n_q, int n_kv, int d);
+// Smallest group size that takes the wide kernel (0 restores the default).
+void set_decode_wide_min_group(int g);
+int decode_wide_min_group();
+hipError_t launch_decode_wide(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
+                              const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
+                              int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
+                              int wg_override, hipStream_t st);
 
 }  // namespace gqa

@@ -275,7 +275,7 @@ const char* gqa_status_string(int status);
  * the launch stream; gqa_profile_read synchronises those events and returns
  * the summed device time and launch count of one kernel kind.
  *   kind: 0 rope_append, 1 decode split-K partials, 2 decode combine,
- *         3 prefill, 4 single-launch decode step.
+ *         3 prefill, 4 single-launch decode step, 5 wide-group decode.
  * Not thread-safe; for single-threaded benchmark drivers.
  */
 int gqa_profile_enable(int on);
@@ -298,6 +298,17 @@ int gqa_set_decode_workgroups(int n);
  * Returns GQA_OK or GQA_ERR_INVALID_ARG.
  */
 int gqa_set_decode_schedule(int static_permille, int chunk_tiles);
+
+/*
+ * Path override for tests and tuning: the smallest group size g = n_q / n_kv
+ * that gqa_decode_attn(_ex) hands to its wide-group kernel (both products on
+ * the matrix cores, every K/V row read once for all g heads; taken only for
+ * g <= 64 and n_kv <= 64).  Smaller groups use the split-K kernel, which reads
+ * K/V once per 16 heads and is the faster one for g <= 8.  0 restores the
+ * default (16); a value above 64 turns the wide kernel off.  Results agree between the paths within the attention
+ * tolerance.  Returns the value in effect.
+ */
+int gqa_set_decode_wide_min_group(int g);
 
 #ifdef __cplusplus
 }

@@ -271,3 +271,11 @@ def test_every_entry_point_checks_the_slab_size():
     assert prefill(**big) == INV
     assert append(**big) == INV
     assert step(**big) == INV
+
+
+def test_wide_group_override():
+    assert gq.gqa_set_decode_wide_min_group(40) == 40
+    assert gq.gqa_set_decode_wide_min_group(0) == 16
+    L = gq.lib()
+    # the decode workspace also covers the wide-group kernel for MQA shapes
+    assert L.gqa_decode_workspace_bytes(16, 64, 1, 128, 8192) >= 256 + 16 * 32 * 64 * 132 * 4

@@ -591,3 +591,79 @@ def test_graph_replays_match_eager():
         three()  # eager work between replays
         torch.cuda.synchronize()
     assert int(ws1[:256].view(torch.int32).abs().sum()) == 0 and int(ws3[:256].view(torch.int32).abs().sum()) == 0
+
+
+# ---------------------------------------------------------------- wide query groups (g > 16, MQA)
+
+WIDE_CASES = [
+    # B, n_q, n_kv, d, S, past, theta, layout, scaling
+    (2, 32, 1, 128, 600, [599, 0], 5.0e5, "interleaved", None),               # g = 32, L = 1
+    (3, 64, 1, 128, 1100, [63, 64, 1099], 5.0e5, "interleaved", SCALED),      # g = 64, tile edges
+    (2, 40, 1, 64, 300, [200, 5], 1.0e4, "half", None),                       # g = 40: padded head block
+    (2, 34, 2, 128, 500, [499, 130], 5.0e5, "interleaved", None),             # g = 17
+    (4, 48, 2, 64, 400, [399, 1, 64, 250], 1.0e4, "interleaved", None),       # g = 24
+    (9, 256, 8, 128, 200, [199, 3, 64, 100, 150, 7, 63, 128, 77], 5.0e5, "interleaved", None),  # two launch slices
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}g{c[1]//c[2]}d{c[3]}")
+def test_wide_group_decode(case):
+    say(f"wide decode {case}")
+    out, ref, _ = run_decode_e2e(case, seed=1500 + case[1])
+    check_out(out, ref, "wide-group decode")
+
+
+def test_wide_group_decode_window_sinks_and_paths():
+    """Window, sinks and learned sinks on the wide kernel; it agrees with the split-K path; calls repeat bit for bit."""
+    B, n_q, n_kv, d, S, past, W, NS = 2, 64, 1, 128, 3000, [2999, 1500], 256, 4
+    say("wide decode window + paths")
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=1601)
+    for b in range(B):
+        kc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 1610 + b))
+        vc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 1620 + b))
+    sinks = np.random.default_rng(3).standard_normal(n_q).astype(np.float32)
+    sk = torch.from_numpy(sinks).to(DEV)
+    qd, kd, vd, pl = dev(q), dev(kc), dev(vc), past_dev(past)
+    ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    o1 = gq.gqa_decode_attn(qd, kd, vd, pl, max(past), workspace=ws, window=W, n_sink=NS, sink_logits=sk)
+    o2 = gq.gqa_decode_attn(qd, kd, vd, pl, max(past), workspace=ws, window=W, n_sink=NS, sink_logits=sk)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    check_out(synth.bits(o1), ref, "wide-group decode under a window")
+    gq.gqa_set_decode_wide_min_group(65)  # split-K path for the same call
+    try:
+        o3 = gq.gqa_decode_attn(qd, kd, vd, pl, max(past), workspace=ws, window=W, n_sink=NS, sink_logits=sk)
+        torch.cuda.synchronize()
+    finally:
+        gq.gqa_set_decode_wide_min_group(0)
+    check_out(synth.bits(o3), ref, "split-K decode, same shape")
+    assert (o1.float() - o3.float()).abs().max().item() <= 2 ** -7
+
+
+def test_wide_group_kernel_on_small_groups():
+    """The wide kernel also serves g <= 16 when asked (padded head blocks)."""
+    case = (3, 32, 8, 128, 700, [699, 64, 300], 5.0e5, "interleaved", None)
+    say("wide kernel at g = 4")
+    gq.gqa_set_decode_wide_min_group(2)
+    try:
+        out, ref, _ = run_decode_e2e(case, seed=1700)
+    finally:
+        gq.gqa_set_decode_wide_min_group(0)
+    check_out(out, ref, "wide kernel, g = 4")
+
+
+@pytest.mark.parametrize("case", [(2, 16, 1, 128, 300, [200, 1], 5.0e5, "interleaved", None),
+                                  (2, 32, 1, 128, 600, [599, 70], 5.0e5, "half", None),
+                                  (2, 64, 2, 64, 300, [299, 64], 1.0e4, "interleaved", SCALED)],
+                         ids=lambda c: f"g{c[1]//c[2]}d{c[3]}")
+def test_split_k_path_for_large_groups(case):
+    """Groups of 16 and more default to the wide kernel; the split-K path (head chunks of 16) stays correct."""
+    say(f"split-K for large groups {case}")
+    gq.gqa_set_decode_wide_min_group(65)
+    try:
+        out, ref, _ = run_decode_e2e(case, seed=1800 + case[1])
+    finally:
+        gq.gqa_set_decode_wide_min_group(0)
+    check_out(out, ref, "split-K, large group")
