@@ -205,7 +205,9 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = key0 + 16 * mb + 4 * lq + i;
-                        if (key > lim || (key <= wlo && key >= n_sink)) sacc[mb][nb][i] = -INFINITY;
+                        // bitwise, not short-circuit: a select per score instead of a branch
+                        const bool hide = (key > lim) | ((key <= wlo) & (key >= n_sink));
+                        sacc[mb][nb][i] = hide ? -INFINITY : sacc[mb][nb][i];
                     }
             }
         }
