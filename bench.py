@@ -16,6 +16,14 @@ per launch from the committed rocprofv3 byte-counter summary under profiles/
 (null once the decode kernel sources differ from the ones it was taken on).
 cpu_baseline = the fp64
 oracle on a bounded sample of the same workload, on this host.
+
+extra (skipped with --no-extra): chunked prefill TFLOP/s (B4, T512 on
+past_len 2048); the 70B-shaped scaled-RoPE decode (B64, 64/8 heads, 80 calls);
+small-batch decode latency (tiny 6/2-head case and one Llama-3.1-8B layer),
+rope_append + decode_attn against the single-launch gqa_decode_step; and
+wide-group decode (B16 64/1 and B32 32/2 heads), the wide kernel against the
+split-K path on the same call.  The small-batch and wide legs time HIP graphs
+of 20 calls replayed back to back, so host launch overhead is excluded.
 """
 
 import argparse
