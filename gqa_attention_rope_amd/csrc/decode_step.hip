@@ -395,8 +395,25 @@ int decode_step_splits(int B, int n_kv, int max_past_len, int window, int n_sink
     return n < 1 ? 1 : (int)n;
 }
 
+// Groups of 16 and more heads run the step as rope_append followed by the
+// wide-group decode kernel (both products on MFMA), which is several times
+// faster there than this kernel's VALU products.  That route keeps the rotated
+// q and the wide kernel's records after the counter region, which stays zero.
+static bool step_takes_wide_route(int n_q, int n_kv) {
+    const int g = n_q / n_kv;
+    return g >= decode_wide_min_group() && g <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS;
+}
+static size_t step_qrot_bytes(int B, int n_q, int d) { return ((size_t)B * n_q * d * 2 + 255) / 256 * 256; }
+
 size_t decode_step_workspace_bytes(int B, int n_q, int n_kv, int d) {
-    return step_counter_bytes(B, n_kv) + (size_t)B * n_q * DECODE_STEP_MAX_SPLITS * (d + 4) * sizeof(float);
+    size_t need = step_counter_bytes(B, n_kv) + (size_t)B * n_q * DECODE_STEP_MAX_SPLITS * (d + 4) * sizeof(float);
+    const int g = n_q / n_kv;
+    if (g <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS) {  // any threshold may send the shape there
+        const size_t wide = step_counter_bytes(B, n_kv) + step_qrot_bytes(B, n_q, d) +
+                            DECODE_WS_HEADER_FLOATS * sizeof(float) + decode_wide_record_bytes(B, n_q, n_kv, d);
+        if (wide > need) need = wide;
+    }
+    return need;
 }
 
 hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
@@ -404,6 +421,16 @@ hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const ui
                               uint16_t* q_rot, void* ws, int B, int n_q, int n_kv, int d, int S, const RopeDev& rope,
                               float scale, int window, int n_sink, const float* sink_logits, hipStream_t st) {
     const int g = n_q / n_kv;
+    if (step_takes_wide_route(n_q, n_kv)) {
+        char* base = static_cast<char*>(ws) + step_counter_bytes(B, n_kv);
+        uint16_t* qr = q_rot ? q_rot : reinterpret_cast<uint16_t*>(base);
+        float* wws = reinterpret_cast<float*>(base + step_qrot_bytes(B, n_q, d));
+        hipError_t e = launch_rope_append(q, qr, k_new, v_new, k_cache, v_cache, past_len, max_past_len, B, n_q, n_kv,
+                                          1, d, S, rope, st);
+        if (e != hipSuccess) return e;
+        return launch_decode_wide(qr, k_cache, v_cache, past_len, max_past_len, out, wws, B, n_q, n_kv, d, S, scale,
+                                  window, n_sink, sink_logits, 0, st);
+    }
     const int nsplit = decode_step_splits(B, n_kv, max_past_len, window, n_sink);
     int* counters = static_cast<int*>(ws);
     float* recs = reinterpret_cast<float*>(static_cast<char*>(ws) + step_counter_bytes(B, n_kv));

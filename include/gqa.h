@@ -241,7 +241,11 @@ int gqa_prefill_attn_ex(const void* q_rot, const void* k_cache, const void* v_ca
  * logits of gqa_attn_opts).  The new row enters the attention from the
  * kernel's registers, so the result never depends on when the append lands.
  * The splits of each (sequence, KV head) are merged by the last one to
- * finish, in split order: bitwise reproducible for a given shape.
+ * finish, in split order: bitwise reproducible for a given shape.  Groups of
+ * g >= 16 heads (the threshold of gqa_set_decode_wide_min_group) run instead
+ * as gqa_rope_append followed by the wide-group decode kernel, three launches
+ * whose matrix-core products beat one launch's vector arithmetic there; the
+ * results and the cache writes are the same.
  *
  *   q, k_new, v_new in [B, n_q | n_kv, 1, d] bf16 (q and k unrotated)
  *   k_cache, v_cache in/out [B, n_kv, S, d] bf16; row past_len[b] is written

@@ -667,3 +667,18 @@ def test_split_k_path_for_large_groups(case):
     finally:
         gq.gqa_set_decode_wide_min_group(0)
     check_out(out, ref, "split-K, large group")
+
+
+@pytest.mark.parametrize("thr", [65, 0], ids=["single_launch", "wide_route"])
+def test_decode_step_large_group_both_routes(thr):
+    """Large groups: the single-launch kernel (forced) and the rope_append + wide-kernel route agree with the oracle."""
+    case = (2, 64, 1, 128, 900, [899, 130], 5.0e5, "half", NTK8, 64, 100, 4, True)
+    say(f"decode_step large group, threshold {thr}")
+    gq.gqa_set_decode_wide_min_group(thr)
+    try:
+        out, ref, (q_rot, q_ref, kc_d, kc_ref, vc_d, vc_ref, kc_in) = run_step(case, seed=1900)
+    finally:
+        gq.gqa_set_decode_wide_min_group(0)
+    check_out(synth.bits(out), ref, "decode_step, large group")
+    assert max_ulp(synth.bits(q_rot), q_ref) <= 1
+    assert np.array_equal(synth.bits(vc_d), vc_ref)
