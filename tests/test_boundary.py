@@ -242,6 +242,7 @@ def step(o=None, **kw):
     (dict(d=96), HD), (dict(maxp=64, S=64), RNG), (dict(maxp=-1), RNG), (dict(wsb=0), WS),
     (dict(n_q=130, n_kv=2), INV), (dict(scale=float("nan")), INV), (dict(rope=rope(rdim=24)), INV),
     (dict(rope=rope(scaled=4, factor=0.5)), INV), (dict(S=1 << 23, maxp=10), INV),
+    (dict(B=65536), INV), (dict(n_q=65536 * 2, n_kv=65536), INV),
 ])
 def test_decode_step_validation(kw, code):
     assert step(**kw) == code

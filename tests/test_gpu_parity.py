@@ -682,3 +682,40 @@ def test_decode_step_large_group_both_routes(thr):
     check_out(synth.bits(out), ref, "decode_step, large group")
     assert max_ulp(synth.bits(q_rot), q_ref) <= 1
     assert np.array_equal(synth.bits(vc_d), vc_ref)
+
+
+# ---------------------------------------------------------------- launch slicing at the batch limits
+
+def test_decode_batch_beyond_one_launch():
+    """More sequences than one split-K launch takes (2048): the batch runs in slices."""
+    B, n_q, n_kv, d, S = 2100, 8, 2, 64, 64
+    past = [int(x) for x in np.random.default_rng(5).integers(0, S - 1, size=B)]
+    say("decode B = 2100")
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=2001)
+    out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past))
+    torch.cuda.synchronize()
+    got = synth.bits(out)
+    pick = [0, 1, 2047, 2048, 2049, B - 1]
+    ref = attend(q[pick], kc[pick], vc[pick], [past[i] for i in pick], n_kv)
+    check_out(got[pick], ref, "decode, sliced batch")
+
+
+def test_rope_and_prefill_batch_beyond_grid_limit():
+    """More sequences than one grid dimension holds (65535): rope_append and prefill run in slices."""
+    B, n_q, n_kv, T, d, S = 65537, 2, 1, 2, 64, 8
+    past = [int(x) for x in np.random.default_rng(6).integers(0, S - T + 1, size=B)]
+    say("rope_append + prefill B = 65537")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=2002)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), 1.0e4)
+    out = gq.gqa_prefill_attn(q_rot, kc_d, vc_d, pl, max(past))
+    torch.cuda.synchronize()
+    pick = [0, 1, 65534, 65535, 65536]
+    pp = [past[i] for i in pick]
+    q_ref, kc_ref, vc_ref = rope_append(q[pick], kn[pick], vn[pick], kc[pick], vc[pick], pp, 1.0e4)
+    assert max_ulp(synth.bits(q_rot)[pick], q_ref) <= 1
+    kc_g = synth.bits(kc_d)[pick]
+    for i, p in enumerate(pp):
+        assert max_ulp(kc_g[i][:, p:p + T], kc_ref[i][:, p:p + T]) <= 1
+    ref = attend(q_ref, kc_ref, vc_ref, pp, n_kv)
+    check_out(synth.bits(out)[pick], ref, "prefill, sliced batch")
