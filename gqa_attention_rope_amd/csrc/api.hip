@@ -62,17 +62,24 @@ namespace gqa {
 
 void prof_begin(int kind, hipStream_t st) {
     if (!g_prof_on) return;
-    hipEvent_t e;
+    hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return;
-    hipEventRecord(e, st);
+    if (hipEventRecord(e, st) != hipSuccess) {  // no timing for this launch
+        (void)hipEventDestroy(e);
+        return;
+    }
     g_pending[kind] = e;
 }
 
 void prof_end(int kind, hipStream_t st) {
     if (!g_prof_on || !g_pending[kind]) return;
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
-    hipEventRecord(e, st);
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess || hipEventRecord(e, st) != hipSuccess) {
+        if (e) (void)hipEventDestroy(e);
+        (void)hipEventDestroy(g_pending[kind]);
+        g_pending[kind] = nullptr;
+        return;
+    }
     g_prof[kind].push_back(EvPair{g_pending[kind], e});
     g_pending[kind] = nullptr;
 }
@@ -295,12 +302,12 @@ int gqa_profile_read(int kind, double* total_ms, long long* launches) {
 int gqa_profile_reset(void) {
     for (int k = 0; k < gqa::K_KINDS; ++k) {
         for (const EvPair& p : g_prof[k]) {
-            hipEventDestroy(p.a);
-            hipEventDestroy(p.b);
+            (void)hipEventDestroy(p.a);
+            (void)hipEventDestroy(p.b);
         }
         g_prof[k].clear();
         if (g_pending[k]) {
-            hipEventDestroy(g_pending[k]);
+            (void)hipEventDestroy(g_pending[k]);
             g_pending[k] = nullptr;
         }
     }
