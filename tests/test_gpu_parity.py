@@ -719,3 +719,33 @@ def test_rope_and_prefill_batch_beyond_grid_limit():
         assert max_ulp(kc_g[i][:, p:p + T], kc_ref[i][:, p:p + T]) <= 1
     ref = attend(q_ref, kc_ref, vc_ref, pp, n_kv)
     check_out(synth.bits(out)[pick], ref, "prefill, sliced batch")
+
+
+@pytest.mark.parametrize("case", [(2, 64, 1, 9, 128, 300, [120, 0], 5.0e5, "interleaved", None),
+                                  (1, 32, 1, 70, 64, 400, [300], 1.0e4, "half", None),
+                                  (2, 48, 2, 5, 128, 200, [64, 190], 5.0e5, "interleaved", SCALED)],
+                         ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}T{c[3]}d{c[4]}")
+def test_prefill_wide_groups(case):
+    """Prefill with many query heads per KV head (MQA and g = 24, 32): few positions per workgroup."""
+    B, n_q, n_kv, T, d, S, past, theta, layout, scaling = case
+    say(f"prefill wide group {case}")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=2100 + n_q)
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
+    ref = attend(q_ref, kc_ref, vc_ref, past, n_kv)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling)
+    out = gq.gqa_prefill_attn(q_rot, kc_d, vc_d, pl, max(past))
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, "prefill, wide group")
+
+
+def test_wide_group_decode_d64_window():
+    B, n_q, n_kv, d, S, past, W, NS = 3, 32, 1, 64, 2000, [1999, 40, 1000], 300, 2
+    say("wide decode d64 window")
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=2201)
+    sinks = np.random.default_rng(7).standard_normal(n_q).astype(np.float32)
+    ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), window=W, n_sink=NS,
+                             sink_logits=torch.from_numpy(sinks).to(DEV))
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, "wide decode, d 64, window")
