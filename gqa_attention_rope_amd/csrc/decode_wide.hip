@@ -1,4 +1,4 @@
-// Decode attention for wide query groups (g > 16 query heads per KV head, up
+// Decode attention for wide query groups (16 or more query heads per KV head, up
 // to multi-query attention with g = n_q): both products on MFMA, each K/V row
 // read once for all g heads.
 //

@@ -86,7 +86,7 @@ hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const ui
                               uint16_t* q_rot, void* ws, int B, int n_q, int n_kv, int d, int S, const RopeDev& rope,
                               float scale, int window, int n_sink, const float* sink_logits, hipStream_t st);
 
-// ---- decode for wide query groups (g > 16: both products on MFMA) -------------
+// ---- decode for wide query groups (g >= 16: both products on MFMA) ------------
 // The decode workspace starts with a header of this many floats (256 bytes)
 // that holds the split-K ticket counter; records follow it.
 constexpr int DECODE_WS_HEADER_FLOATS = 64;
