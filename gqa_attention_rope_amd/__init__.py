@@ -42,6 +42,7 @@ EXPORTED = (
     "gqa_profile_reset",
     "gqa_set_decode_workgroups",
     "gqa_set_decode_schedule",
+    "gqa_set_decode_slot_ratio",
     "gqa_set_decode_wide_min_group",
 )
 
@@ -120,6 +121,8 @@ def lib():
     L.gqa_set_decode_wide_min_group.restype = i32
     L.gqa_set_decode_schedule.argtypes = [i32, i32]
     L.gqa_set_decode_schedule.restype = i32
+    L.gqa_set_decode_slot_ratio.argtypes = [i32]
+    L.gqa_set_decode_slot_ratio.restype = i32
     _lib = L
     return L
 
@@ -363,6 +366,12 @@ def gqa_set_decode_workgroups(n):
 def gqa_set_decode_schedule(static_permille=-1, chunk_tiles=0):
     """Static fraction (per mille) and dynamic chunk size of the decode split; (-1, 0) = defaults."""
     _check(lib().gqa_set_decode_schedule(int(static_permille), int(chunk_tiles)))
+
+
+def gqa_set_decode_slot_ratio(ratio_permille=0):
+    """Static share of each dispatch slot relative to the next younger one (per mille); 0 = the kernel
+    variant's default.  Returns the override in effect (clamped to [250, 8000]; 0 for the defaults)."""
+    return int(lib().gqa_set_decode_slot_ratio(int(ratio_permille)))
 
 
 def gqa_set_decode_wide_min_group(g=0):

@@ -324,6 +324,14 @@ int gqa_set_decode_wide_min_group(int g) {
     return gqa::decode_wide_min_group();
 }
 
+int gqa_set_decode_slot_ratio(int ratio_permille) {
+    int r = ratio_permille;
+    if (r > 0) r = r < 250 ? 250 : (r > 8000 ? 8000 : r);
+    else r = 0;
+    gqa::set_decode_slot_ratio(r);
+    return gqa::decode_slot_ratio();
+}
+
 int gqa_set_decode_schedule(int static_permille, int chunk_tiles) {
     if (static_permille < 0 && chunk_tiles <= 0) {
         gqa::set_decode_schedule(gqa::DECODE_DEFAULT_STATIC_PM, gqa::DECODE_DEFAULT_CHUNK);

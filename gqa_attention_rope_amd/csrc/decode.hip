@@ -119,11 +119,70 @@ __device__ void tile_prefix(const int32_t* past_len, int B, int pmax, int window
     __syncthreads();
 }
 
-// workgroup w of G covers tiles [w*T/G, (w+1)*T/G)
-__device__ __forceinline__ long long share_begin(long long w, long long T, long long G) { return (w * T) / G; }
-// the workgroup whose share holds tile tau: the largest w with share_begin(w) <= tau
-__device__ __forceinline__ long long owner_of(long long tau, long long T, long long G) {
-    return ((tau + 1) * G - 1) / T;
+// Static shares weighted by dispatch slot.  The hardware hands out a grid one
+// workgroup per CU per round, so workgroup w is the (w / n_cu)-th resident of
+// its CU.  Older residents win instruction issue and stream faster (measured
+// at three per CU: about 1.5x per slot), so equal shares would leave the
+// youngest finishing long after the rest; slot s gets a share proportional to
+// its weight.  Shares are 32.32 fixed-point fractions of the static tiles:
+// workgroup w starts at floor(Ts F(w) / 2^32), where F(w) is the fraction of
+// all workgroups before it.  Both kernels evaluate this with multiplies only
+// (no integer division on the combine's critical path).
+struct Shares {
+    int n_cu;                          // workgroups per dispatch round
+    int ns;                            // rounds (slots) in the grid, 1 .. 4
+    int G;                             // workgroups in the grid
+    unsigned long long f1, f2, f3;     // fraction before slot 1, 2, 3 (before slot 0: 0)
+    unsigned long long g0, g1, g2, g3; // fraction of one workgroup of slot 0 .. 3
+};
+// Fields selected without indexing: the struct stays in scalar registers
+// (an indexed array member would be copied to scratch memory).
+__device__ __forceinline__ unsigned long long frac_before_slot(const Shares& sh, int s) {
+    return s <= 0 ? 0ull : (s == 1 ? sh.f1 : (s == 2 ? sh.f2 : sh.f3));
+}
+__device__ __forceinline__ unsigned long long frac_per_wg(const Shares& sh, int s) {
+    return s == 0 ? sh.g0 : (s == 1 ? sh.g1 : (s == 2 ? sh.g2 : sh.g3));
+}
+// first tile of workgroup w's static share (w = G gives Ts); Ts < 2^31 and
+// F <= 2^32, so the product fits in 64 bits
+__device__ __forceinline__ long long share_begin(int w, long long Ts, const Shares& sh) {
+    if (w >= sh.G) return Ts;
+    int s = w / sh.n_cu;
+    if (s > sh.ns - 1) s = sh.ns - 1;
+    const unsigned long long f = frac_before_slot(sh, s) + (unsigned long long)(w - s * sh.n_cu) * frac_per_wg(sh, s);
+    return (long long)(((unsigned long long)Ts * f) >> 32);
+}
+// a * b <= x, exactly (the product may exceed 64 bits)
+__device__ __forceinline__ bool prod_le(unsigned long long a, unsigned long long b, unsigned long long x) {
+    return __umul64hi(a, b) == 0 && a * b <= x;
+}
+// The workgroup whose share holds tile tau < Ts: the largest w < G with
+// share_begin(w) <= tau, i.e. with Ts F(w) < R = (tau + 1) 2^32.  The slot is
+// the last one whose first workgroup qualifies; inside it F grows by a fixed
+// step E / Ts per workgroup, so the count is floor((R - Ts F(first) - 1) / E),
+// estimated in fp64 and made exact with integer checks.
+__device__ __forceinline__ long long owner_of(long long tau, long long Ts, const Shares& sh) {
+    const unsigned long long R = (unsigned long long)(tau + 1) << 32;
+    const unsigned long long T = (unsigned long long)Ts;
+    int s = 0;
+#pragma unroll
+    for (int k = 1; k < 4; ++k)
+        if (k < sh.ns && T * frac_before_slot(sh, k) < R) s = k;
+    const int first = s * sh.n_cu;
+    const int cnt = (sh.G - first) < sh.n_cu ? (sh.G - first) : sh.n_cu;
+    const unsigned long long X = R - T * frac_before_slot(sh, s) - 1;
+    const unsigned long long E = T * frac_per_wg(sh, s);
+    double qd = floor((double)X / (double)E);
+    unsigned long long q = qd > 0.0 ? (unsigned long long)qd : 0ull;
+    // the estimate is off by at most one
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (q > 0 && !prod_le(q, E, X)) --q;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (prod_le(q + 1, E, X)) ++q;
+    const long long k = (long long)q < cnt - 1 ? (long long)q : cnt - 1;
+    return first + k;
 }
 
 // Position of one tile in the concatenated tile list: sequence b, segment sj
@@ -184,7 +243,7 @@ template <int D, int HGW, int NHG>
 __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ past_len, int pmax, float* __restrict__ ws, int B, int n_q, int n_kv, int S, int nhc,
-    float scale_log2, int static_pm, int chunk, int window, int n_sink) {
+    float scale_log2, int static_pm, int chunk, int window, int n_sink, Shares shares) {
     using C = Cfg<D, HGW, NHG>;
     constexpr int KB = C::KB, KS = C::KS;
     constexpr int DPL = D / 64;                  // value dims each lane accumulates
@@ -276,8 +335,8 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     Cursor ld;
     ld.b = 0; ld.sj = 0; ld.tt = 0; ld.nt = 1; ld.L = 1; ld.nst = 1; ld.at0 = 1; ld.w0 = 0;
     ld.hc = 0; ld.seg = 0; ld.qoff = 0; ld.kvoff = 0;
-    const int tau_w = (int)share_begin(w, sc.Ts, G);
-    int ld_left = (int)share_begin(w + 1, sc.Ts, G) - tau_w;
+    const int tau_w = (int)share_begin(w, sc.Ts, shares);
+    int ld_left = (int)share_begin(w + 1, sc.Ts, shares) - tau_w;
     int ld_rid = w;
     if (ld_left > 0) ld = cursor_at(tau_w);
     int nx_tau = 0, nx_len = 0, nx_rid = 0;
@@ -620,13 +679,32 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
 // together; the four states then merge in wave order through LDS.  Block
 // (0, 0) also clears the ticket counter, so the next call starts from zero.
 constexpr int CMB_WAVES = 4;
+// The records of one segment, in merge order: the static shares of
+// workgroups w_lo .. w_lo + n_st - 1, then consecutive chunk records.
+struct RecordList {
+    int nrec, n_st, w_lo, seg, dyn0;  // dyn0: slot of the first chunk record, less seg
+    long long Ts;
+};
+// Slot of record idx (record 0's for idx >= nrec) and whether it holds data:
+// a static share can be empty when the weights make it shorter than a tile.
+__device__ __forceinline__ int record_slot(const RecordList rl, int idx, const Shares sh, bool& use) {
+    use = idx < rl.nrec;
+    if (!use) idx = 0;
+    if (idx < rl.n_st) {
+        const int w = rl.w_lo + idx;
+        use = use && share_begin(w, rl.Ts, sh) < share_begin(w + 1, rl.Ts, sh);
+        return w + rl.seg;
+    }
+    return rl.dyn0 + (idx - rl.n_st) + rl.seg;
+}
 template <int D>
 __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* __restrict__ ws,
                                                                         const int32_t* __restrict__ past_len,
                                                                         int pmax, uint16_t* __restrict__ out, int B,
                                                                         int n_q, int n_kv, int nhc, int gc, int G,
                                                                         int static_pm, int chunk, int window,
-                                                                        int n_sink, const float* sink_logits) {
+                                                                        int n_sink, const float* sink_logits,
+                                                                        Shares shares) {
     constexpr int DPL = D / 64;  // dims per lane
     constexpr int REC = D + 4;
     constexpr int RB = 8;        // records per wave and batch
@@ -667,8 +745,8 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
     const long long s_end = end < sc.Ts ? end : sc.Ts;
     long long w_lo = 0, n_st = 0;
     if (start < s_end) {
-        w_lo = owner_of(start, sc.Ts, G);
-        n_st = owner_of(s_end - 1, sc.Ts, G) - w_lo + 1;
+        w_lo = owner_of(start, sc.Ts, shares);
+        n_st = owner_of(s_end - 1, sc.Ts, shares) - w_lo + 1;
     }
     // chunks t_lo..t_lo + n_dy - 1
     const long long d_start = start > sc.Ts ? start : sc.Ts;
@@ -682,16 +760,7 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
 
     // record idx is used if it exists and (static) its workgroup had a non-empty share;
     // record 0 always exists, so unused entries read it and are ignored
-    auto slot_of = [&](int idx, bool& use) -> long long {
-        use = idx < nrec;
-        if (!use) idx = 0;
-        if (idx < n_st) {
-            const long long w = w_lo + idx;
-            use = use && share_begin(w, sc.Ts, G) < share_begin(w + 1, sc.Ts, G);
-            return w + seg;
-        }
-        return dyn_slot0 + t_lo + (idx - n_st) + seg;
-    };
+    const RecordList rl{nrec, (int)n_st, (int)w_lo, (int)seg, (int)(dyn_slot0 + t_lo), sc.Ts};
 
     float M = -INFINITY, L = 0.f, acc[DPL];
 #pragma unroll
@@ -700,10 +769,15 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
         float2 ml[RB];
         float ov[RB][DPL];
         bool use[RB];
+        // lane u (< RB) locates record u of the batch once; the wave reads the results back
+        bool use_l;
+        const int slot_l = record_slot(rl, base + CMB_WAVES * (lane % RB), shares, use_l);
+        const unsigned long long use_mask = __builtin_amdgcn_ballot_w64(use_l);
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
-            const float* rp =
-                recs + (size_t)slot_of(base + CMB_WAVES * u, use[u]) * slot_floats + (size_t)hl * REC;
+            use[u] = ((use_mask >> u) & 1ull) != 0;
+            const int slot_u = __builtin_amdgcn_readlane(slot_l, u);
+            const float* rp = recs + (size_t)slot_u * slot_floats + (size_t)hl * REC;
             ml[u] = *reinterpret_cast<const float2*>(rp);
 #pragma unroll
             for (int x = 0; x < DPL; ++x) ov[u][x] = rp[4 + DPL * lane + x];
@@ -756,11 +830,12 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
 template <int D, int HGW, int NHG>
 hipError_t launch_partial_t(int G, const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                             const int32_t* past_len, int pmax, float* ws, int B, int n_q, int n_kv, int S, int nhc,
-                            float scale_log2, int static_pm, int chunk, int window, int n_sink, hipStream_t st) {
+                            float scale_log2, int static_pm, int chunk, int window, int n_sink,
+                            const Shares& shares, hipStream_t st) {
     const size_t dyn = (size_t)(B + 1) * sizeof(int);
     hipLaunchKernelGGL((decode_partial_kernel<D, HGW, NHG>), dim3(G), dim3(THREADS), dyn, st, q_rot, k_cache,
                        v_cache, past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2, static_pm, chunk, window,
-                       n_sink);
+                       n_sink, shares);
     return hipGetLastError();
 }
 
@@ -775,13 +850,17 @@ int occupancy_t(int B) {
 
 using occ_fn = int (*)(int);
 using partial_fn = hipError_t (*)(int, const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int, float*,
-                                  int, int, int, int, int, float, int, int, int, int, hipStream_t);
+                                  int, int, int, int, int, float, int, int, int, int, const Shares&, hipStream_t);
 
 struct Variant {
     int hgw, nhg;
     partial_fn fn128, fn64;
     occ_fn occ128, occ64;
 };
+// Default share ratio between dispatch slots, by head groups per workgroup:
+// measured best at 1.5 for one head group (g = 4, 32/8 heads) and 1.2 for two
+// (g = 8, 64/8 heads); the others take 1.2.
+int default_slot_ratio(const Variant& v) { return v.nhg == 1 ? 1500 : 1200; }
 
 #define GQA_VARIANT(H, N)                                                                                   \
     Variant {                                                                                               \
@@ -800,6 +879,44 @@ const Variant& pick_variant(int g) {
 
 int g_static_pm = DECODE_DEFAULT_STATIC_PM;
 int g_chunk = DECODE_DEFAULT_CHUNK;
+int g_slot_ratio_pm = 0;  // 0: the kernel variant's default
+
+// Share weights for a grid of G workgroups on n_cu CUs: slot s (of ns) weighs
+// ratio^(ns - 1 - s), the youngest slot 1 (in units of 1/1000).
+Shares make_shares(int G, int n_cu, int ratio_pm) {
+    static_assert(DECODE_MAX_SLOTS == 4, "the share struct holds four slots");
+    if (n_cu < 1) n_cu = 1;
+    // more rounds than weights (a small GPU with a large grid): widen the rounds
+    if ((G + n_cu - 1) / n_cu > DECODE_MAX_SLOTS) n_cu = (G + DECODE_MAX_SLOTS - 1) / DECODE_MAX_SLOTS;
+    int ns = (G + n_cu - 1) / n_cu;
+    if (ns < 1) ns = 1;
+    unsigned long long wt[DECODE_MAX_SLOTS] = {0, 0, 0, 0}, cnt[DECODE_MAX_SLOTS] = {0, 0, 0, 0};
+    double w = 1000.0;
+    for (int s = ns - 1; s >= 0; --s) {
+        wt[s] = (unsigned long long)(w + 0.5);
+        w = w * ratio_pm / 1000.0;
+        if (w > 1.0e6) w = 1.0e6;  // bounded: wt << 32 stays below 2^52
+    }
+    unsigned long long total = 0;
+    for (int s = 0; s < ns; ++s) {
+        cnt[s] = (s + 1) * n_cu <= G ? n_cu : G - s * n_cu;
+        total += cnt[s] * wt[s];
+    }
+    // per-workgroup fractions rounded down, so the fractions sum to at most 2^32
+    unsigned long long g[DECODE_MAX_SLOTS], f[DECODE_MAX_SLOTS + 1];
+    f[0] = 0;
+    for (int s = 0; s < DECODE_MAX_SLOTS; ++s) {
+        g[s] = (wt[s] << 32) / total;
+        f[s + 1] = f[s] + cnt[s] * g[s];
+    }
+    Shares sh;
+    sh.n_cu = n_cu;
+    sh.ns = ns;
+    sh.G = G;
+    sh.f1 = f[1]; sh.f2 = f[2]; sh.f3 = f[3];
+    sh.g0 = g[0]; sh.g1 = g[1]; sh.g2 = g[2]; sh.g3 = g[3];
+    return sh;
+}
 
 }  // namespace
 
@@ -807,6 +924,9 @@ void set_decode_schedule(int static_permille, int chunk_tiles) {
     g_static_pm = static_permille;
     g_chunk = chunk_tiles;
 }
+
+void set_decode_slot_ratio(int ratio_permille) { g_slot_ratio_pm = ratio_permille; }
+int decode_slot_ratio() { return g_slot_ratio_pm; }
 
 DecodePlan decode_plan(int n_q, int n_kv, int d) {
     const int g = n_q / n_kv;
@@ -885,6 +1005,7 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
     if (G < 1) G = 1;
     const float scale_log2 = scale * LOG2E;
     const int spm = g_static_pm;
+    const Shares shares = make_shares(G, cu_count, g_slot_ratio_pm > 0 ? g_slot_ratio_pm : default_slot_ratio(v));
 
     for (int b0 = 0; b0 < B; b0 += DECODE_MAX_B) {
         const int nb = (B - b0) < DECODE_MAX_B ? (B - b0) : DECODE_MAX_B;
@@ -904,7 +1025,7 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
 
         prof_begin(K_DECODE_PARTIAL, st);
         hipError_t e = (d == 128 ? v.fn128 : v.fn64)(G, q, kc, vc, pl, max_past_len, ws, nb, n_q, n_kv, S, p.nhc,
-                                                     scale_log2, spm, (int)chunk, window, n_sink, st);
+                                                     scale_log2, spm, (int)chunk, window, n_sink, shares, st);
         prof_end(K_DECODE_PARTIAL, st);
         if (e != hipSuccess) return e;
 
@@ -912,11 +1033,11 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
         if (d == 128)
             hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl,
                                max_past_len, o, nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk, window, n_sink,
-                               sink_logits);
+                               sink_logits, shares);
         else
             hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl,
                                max_past_len, o, nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk, window, n_sink,
-                               sink_logits);
+                               sink_logits, shares);
         prof_end(K_DECODE_COMBINE, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

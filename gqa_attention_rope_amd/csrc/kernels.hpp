@@ -44,12 +44,16 @@ constexpr int DECODE_MAX_B = 2048;
 // Upper bound on the number of split-K workgroups (sizes the workspace).
 constexpr int DECODE_MAX_WG = 2048;
 // Work schedule of the split-K kernel: this many per-mille of the tiles are
-// split into equal static shares, the rest into chunks of DECODE_DEFAULT_CHUNK
+// split into static shares (weighted by dispatch slot), the rest into chunks of DECODE_DEFAULT_CHUNK
 // tiles handed out by a ticket counter (at most DECODE_MAX_CHUNKS chunks; the
 // chunk grows when a launch would need more).
-constexpr int DECODE_DEFAULT_STATIC_PM = 700;
-constexpr int DECODE_DEFAULT_CHUNK = 4;
+constexpr int DECODE_DEFAULT_STATIC_PM = 900;
+constexpr int DECODE_DEFAULT_CHUNK = 3;
 constexpr int DECODE_MAX_CHUNKS = 8192;
+// The static shares are weighted by dispatch slot (the k-th workgroup resident
+// on a CU): each slot's share is a fixed multiple of the next younger one's,
+// by default chosen per kernel variant; at most this many distinct slots.
+constexpr int DECODE_MAX_SLOTS = 4;
 
 struct DecodePlan {
     int hgw;   // query heads per wave (1..4)
@@ -63,6 +67,8 @@ struct DecodePlan {
 DecodePlan decode_plan(int n_q, int n_kv, int d);
 size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d);
 void set_decode_schedule(int static_permille, int chunk_tiles);
+void set_decode_slot_ratio(int ratio_permille);  // 0: per-variant defaults
+int decode_slot_ratio();
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
                          int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,

@@ -296,12 +296,26 @@ int gqa_set_decode_workgroups(int n);
 
 /*
  * Work-schedule override for tests and tuning: static_permille (0..1000) of
- * the decode tiles are split into equal static shares, the rest into chunks of
+ * the decode tiles are split into static shares, the rest into chunks of
  * chunk_tiles (>= 1) tiles handed out dynamically.  (-1, 0) restores the
  * defaults.  Results do not depend on it beyond floating-point rounding.
  * Returns GQA_OK or GQA_ERR_INVALID_ARG.
  */
 int gqa_set_decode_schedule(int static_permille, int chunk_tiles);
+
+/*
+ * Work-split tuning of the decode split-K kernel: the static share of each
+ * workgroup dispatch slot (the k-th workgroup resident on a CU) is
+ * ratio_permille / 1000 times that of the next younger slot.  Older residents
+ * win instruction issue on a CU and stream faster, so equal shares
+ * (ratio_permille = 1000) leave the youngest finishing last.  A value <= 0
+ * restores the defaults, which depend on the kernel variant (1500 when a
+ * workgroup holds one head group, i.e. up to 4 query heads per segment, and
+ * 1200 otherwise); others are
+ * clamped to [250, 8000].  Results do not depend on it beyond floating-point
+ * rounding.  Returns the override in effect, 0 for the defaults.
+ */
+int gqa_set_decode_slot_ratio(int ratio_permille);
 
 /*
  * Path override for tests and tuning: the smallest group size g = n_q / n_kv

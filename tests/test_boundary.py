@@ -154,6 +154,14 @@ def test_decode_workgroup_override_clamps():
     assert gq.gqa_set_decode_workgroups(0) == 0
 
 
+def test_decode_slot_ratio_clamps():
+    assert gq.gqa_set_decode_slot_ratio(0) == 0  # per-variant defaults
+    assert gq.gqa_set_decode_slot_ratio(1000) == 1000
+    assert gq.gqa_set_decode_slot_ratio(10) == 250
+    assert gq.gqa_set_decode_slot_ratio(10 ** 6) == 8000
+    assert gq.gqa_set_decode_slot_ratio(-1) == 0
+
+
 def test_decode_schedule_override_validates():
     assert gq.gqa_set_decode_schedule(700, 2) is None
     assert gq.gqa_set_decode_schedule(0, 1) is None

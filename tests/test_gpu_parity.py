@@ -188,7 +188,7 @@ DECODE_CASES = [
 ]
 
 
-def run_decode_e2e(case, seed, wg=0, schedule=(-1, 0)):
+def run_decode_e2e(case, seed, wg=0, schedule=(-1, 0), slot_ratio=0):
     B, n_q, n_kv, d, S, past, theta, layout, scaling = case
     q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed)
     q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
@@ -196,6 +196,7 @@ def run_decode_e2e(case, seed, wg=0, schedule=(-1, 0)):
     kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
     gq.gqa_set_decode_workgroups(wg)
     gq.gqa_set_decode_schedule(*schedule)
+    gq.gqa_set_decode_slot_ratio(slot_ratio)
     try:
         q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling)
         out = gq.gqa_decode_attn(q_rot, kc_d, vc_d, pl, max(past))
@@ -203,6 +204,7 @@ def run_decode_e2e(case, seed, wg=0, schedule=(-1, 0)):
     finally:
         gq.gqa_set_decode_workgroups(0)
         gq.gqa_set_decode_schedule()
+        gq.gqa_set_decode_slot_ratio(0)
     return synth.bits(out), ref, (q_rot, kc_d, vc_d, pl)
 
 
@@ -253,6 +255,21 @@ def test_decode_schedule_invariance_and_determinism(wg):
         check_out(got, ref, f"decode wg={wg} schedule={sched}")
         again, _, _ = run_decode_e2e(case, seed=91, wg=wg, schedule=sched)
         assert np.array_equal(again, got), f"schedule {sched}: repeated call differs"
+
+
+@pytest.mark.parametrize("wg", [0, 600, 1100])
+def test_decode_slot_weighted_shares(wg):
+    """Static shares weighted by dispatch slot: equal (1000), the default, steep (3000) and extreme (8000,
+    where the youngest slots get empty shares) ratios, over grids of one to several dispatch rounds, with
+    all-static and mixed splits: same results to the tolerance, bitwise repeatable."""
+    case = (6, 32, 8, 128, 3000, [2999, 0, 700, 1500, 64, 2100], 5.0e5, "interleaved", None)
+    say(f"decode slot-weighted shares wg={wg}")
+    for ratio in (1000, 0, 3000, 8000):
+        for sched in ((1000, 2), (700, 4)):
+            got, ref, _ = run_decode_e2e(case, seed=93, wg=wg, schedule=sched, slot_ratio=ratio)
+            check_out(got, ref, f"decode wg={wg} ratio={ratio} schedule={sched}")
+            again, _, _ = run_decode_e2e(case, seed=93, wg=wg, schedule=sched, slot_ratio=ratio)
+            assert np.array_equal(again, got), f"ratio {ratio} schedule {sched}: repeated call differs"
 
 
 def test_decode_workspace_reuse_leaves_header_zero():
