@@ -13,6 +13,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// Cache-policy operand of the raw buffer load/store builtins: the non-temporal
+// (streaming) hint, emitted as the "nt" modifier on gfx950.
+constexpr int CPOL_NT = 2;
+
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 
 // bf16 in the low / high half of a 32-bit word, widened exactly to fp32

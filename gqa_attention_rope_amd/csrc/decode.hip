@@ -396,10 +396,13 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg_off), (short)0, valid_bytes, RSRC_FLAGS);
         const int soff = uni(at * TILEB);
+        // K/V rows are read once per launch: non-temporal loads (nt) keep them from
+        // displacing the split-K records and other reused lines in the caches
+        // (measured: 108.7 -> 99.5 us for one Llama-3.1-8B layer at B = 32)
 #pragma unroll
         for (int x = 0; x < HALF; ++x) {
-            buf[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + x * THREADS * 16, 0);
-            buf[HALF + x] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + x * THREADS * 16, 0);
+            buf[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, tid * 16, soff + x * THREADS * 16, CPOL_NT);
+            buf[HALF + x] = __builtin_amdgcn_raw_buffer_load_b128(rv, tid * 16, soff + x * THREADS * 16, CPOL_NT);
         }
         {
             const uint16_t* qseg = q_rot + ld.qoff;
