@@ -38,14 +38,26 @@ def max_ulp(a, b):
     return int(np.max(np.abs(ulp_key(a) - ulp_key(b)))) if np.size(a) else 0
 
 
+def half_ulp_bf16(x):
+    """Half the spacing of bf16 values at |x| (8 significant bits): the most that rounding x to bf16 moves it."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
 def check_out(gpu_bits, ref, name):
+    """Attention outputs against the fp64 oracle: max-abs 1e-2 on the computed result, which the output
+    then carries rounded once to bf16 (up to half a bf16 ulp of the reference more), and max-rel 1e-2."""
     g = bf16_to_f64(gpu_bits)
     assert np.all(np.isfinite(g)), f"{name}: non-finite outputs"
     err = np.abs(g - ref)
     rel = err / np.maximum(np.abs(ref), 1e-2)
-    bad = (err > 1e-2) | (rel > 1e-2)
+    bad = (err > 1e-2 + half_ulp_bf16(ref)) | (rel > 1e-2)
     say(f"  {name}: max abs {err.max():.3e}  max rel {rel.max():.3e}  n={err.size}")
-    assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} outside (abs {err.max():.3e}, rel {rel.max():.3e})"
+    if bad.any():
+        i = np.flatnonzero(bad)[0]
+        raise AssertionError(f"{name}: {int(bad.sum())} of {bad.size} outside; first at flat index {i}: "
+                             f"ref {ref.flat[i]:.6g} got {g.flat[i]:.6g} (max abs {err.max():.3e}, "
+                             f"max rel {rel.max():.3e})")
 
 
 def dev(bits):
@@ -189,10 +201,13 @@ DECODE_CASES = [
 
 
 def run_decode_e2e(case, seed, wg=0, schedule=(-1, 0), slot_ratio=0):
+    """rope_append + decode_attn on the GPU.  The rotated rows are checked against the oracle's (q and k
+    within 1 bf16 ulp, v exact); the attention reference is the oracle on the same bf16 inputs the GPU
+    attention read (its rotated q and appended rows), so a permitted 1-ulp rotation difference does not
+    count against the attention tolerance."""
     B, n_q, n_kv, d, S, past, theta, layout, scaling = case
     q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed)
     q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
-    ref = attend(q_ref, kc_ref, vc_ref, past, n_kv)
     kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
     gq.gqa_set_decode_workgroups(wg)
     gq.gqa_set_decode_schedule(*schedule)
@@ -205,6 +220,15 @@ def run_decode_e2e(case, seed, wg=0, schedule=(-1, 0), slot_ratio=0):
         gq.gqa_set_decode_workgroups(0)
         gq.gqa_set_decode_schedule()
         gq.gqa_set_decode_slot_ratio(0)
+    rows_b, rows_p = np.arange(B), np.asarray(past)
+    tb, tp = torch.as_tensor(rows_b, device=DEV), torch.as_tensor(rows_p, device=DEV)
+    qg = synth.bits(q_rot)
+    kg_rows, vg_rows = synth.bits(kc_d[tb, :, tp]), synth.bits(vc_d[tb, :, tp])
+    assert max_ulp(qg, q_ref) <= 1, "rotated q beyond 1 bf16 ulp"
+    assert max_ulp(kg_rows, kc_ref[rows_b, :, rows_p]) <= 1, "rotated k row beyond 1 bf16 ulp"
+    assert np.array_equal(vg_rows, vc_ref[rows_b, :, rows_p]), "appended v row differs"
+    kc_ref[rows_b, :, rows_p] = kg_rows
+    ref = attend(qg, kc_ref, vc_ref, past, n_kv)
     return synth.bits(out), ref, (q_rot, kc_d, vc_d, pl)
 
 
@@ -270,6 +294,17 @@ def test_decode_slot_weighted_shares(wg):
             check_out(got, ref, f"decode wg={wg} ratio={ratio} schedule={sched}")
             again, _, _ = run_decode_e2e(case, seed=93, wg=wg, schedule=sched, slot_ratio=ratio)
             assert np.array_equal(again, got), f"ratio {ratio} schedule {sched}: repeated call differs"
+
+
+def test_decode_many_short_segments():
+    """17600 (sequence, KV head) segments of at most one tile each: a record per segment, ragged one-row
+    to 31-row contexts, outputs up to |4| and more (where a bf16 output rounds by up to 0.0156)."""
+    B, n_q, n_kv, d, S = 1100, 32, 16, 64, 32
+    past = [int(x) for x in np.random.default_rng(6).integers(0, 31, size=B)]
+    case = (B, n_q, n_kv, d, S, past, 1.0e4, "interleaved", None)
+    say(f"decode many segments B{B} n_kv{n_kv}")
+    got, ref, _ = run_decode_e2e(case, seed=99)
+    check_out(got, ref, "decode many segments")
 
 
 def test_decode_workspace_reuse_leaves_header_zero():
