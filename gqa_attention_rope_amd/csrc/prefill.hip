@@ -8,18 +8,22 @@
 //
 // How: a workgroup (4 waves) owns 128 query rows of one (sequence, KV head):
 // up to 128/g positions times the g heads of the group, so every K/V tile it
-// stages serves all heads that share it.  Per 64-key tile:
+// loads serves all heads that share it.  Per 64-key tile:
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = the
 //                  wave's 32 query rows held in registers)
 //   online softmax per query row (each lane holds one query row per 16-row
 //                  block, so only two cross-lane steps are needed)
-//   O^T += V^T P^T (A = V^T from a transposed LDS copy of the V tile,
-//                  B = the softmax weights already in the right lanes, split
-//                  into a bf16 high part and a bf16 remainder so that the
-//                  weights enter the product with ~16 significant bits)
-// Tiles entirely above every row's causal bound are never loaded; tiles that
-// straddle a bound are masked element-wise.  The next tile's global loads are
-// in flight while the current tile is computed.
+//   O^T += V^T P^T (A = V^T read from the row-major V tile with the
+//                  transposing LDS read ds_read_b64_tr_b16, B = the softmax
+//                  weights already in the right lanes, split into a bf16 high
+//                  part and a bf16 remainder so that the weights enter the
+//                  product with ~16 significant bits)
+// K and V tiles go from HBM straight into LDS (range-checked buffer loads with
+// the LDS destination, no register staging), double-buffered: the next
+// tile's loads are in flight while the current one is computed, and one
+// workgroup barrier per tile both publishes the new tile and frees the old
+// buffer.  Tiles entirely above every row's causal bound are never loaded;
+// tiles that straddle a bound are masked element-wise.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,14 +36,25 @@ constexpr int NTHR = 256;     // 4 waves
 constexpr int ROWS = 128;     // query rows per workgroup (32 per wave)
 constexpr float LOG2E_P = 1.4426950408889634f;
 
-// K tile: [64 keys][D] bf16 in 16-byte pieces; piece c of key r sits at c ^ (r mod PPR)
-template <int PPR>
-__device__ __forceinline__ int kpos(int key, int c) {
-    return key * PPR + (c ^ (key & (PPR - 1)));
-}
-// V^T tile: [D dims][64 keys] bf16 in 8-byte units of 4 keys; unit u of dim row d sits at u ^ (d mod 16)
-__device__ __forceinline__ int vt_byte(int dim, int unit) { return dim * 128 + ((unit ^ (dim & 15)) << 3); }
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
+// A range-checked 16-byte-per-lane buffer load whose data goes to LDS (lane i
+// writes m0 + 16 i; lanes past the range write zeros).  Issued as inline asm:
+// through the builtin the compiler guards the later transposed LDS reads of
+// the other buffer with a wait for these loads, which would expose their
+// latency every tile.  The kernel waits for them itself (vmcnt(0) before the
+// barrier that publishes the tile).  The instruction has no register result.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voff, int soff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
+}
+
+// LDS tiles ([64 keys][D] bf16, row-major) are kept in 16-byte pieces; piece c
+// of key row r sits at slot c ^ (r mod PPR).  With this swizzle the K operand
+// reads (16 B per lane: 16 rows x 4 pieces) and the transposed V reads (8 B per
+// lane: 16 rows x 2 pieces) each spread over all banks.
 template <int D>
 __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __restrict__ q_rot,
                                                           const uint16_t* __restrict__ k_cache,
@@ -48,15 +63,17 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ out, int n_q, int n_kv, int T,
                                                           int S, int hpw, int tq, int n_tq, float scale_log2,
                                                           int window, int n_sink, const float* sink_logits) {
-    constexpr int PPR = D / 8;     // 16-byte pieces per key row
-    constexpr int KS = D / 32;     // MFMA k-steps over d
-    constexpr int DB = D / 16;     // 16-dim blocks of the output
-    constexpr int K_LOADS = KT * PPR / NTHR;        // 16-byte K loads per thread
-    constexpr int V_ITEMS = (KT / 2) * PPR / NTHR;  // (key pair, piece) items per thread
-    __shared__ uint4 s_k[KT * PPR];
-    __shared__ __align__(16) unsigned char s_vt[D * 128];
+    constexpr int PPR = D / 8;                 // 16-byte pieces per key row
+    constexpr int KS = D / 32;                 // MFMA k-steps over d
+    constexpr int DB = D / 16;                 // 16-dim blocks of the output
+    constexpr int ROW_B = D * 2;               // bytes per key row
+    constexpr int TILE_B = KT * ROW_B;         // bytes per K (or V) tile
+    constexpr int DMA_N = KT * PPR / NTHR;     // 16-byte pieces per thread, per tensor and tile
+    // K buffers 0 and 1, then V buffers 0 and 1
+    __shared__ __align__(16) unsigned char smem[4 * TILE_B];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int g = n_q / n_kv;
     const int tq_idx = n_tq - 1 - (int)(blockIdx.x % n_tq);  // longest rows first
@@ -119,48 +136,41 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kv_end * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, kv_end * D * 2, 0x00020000);
-    u32x4_t kst[K_LOADS];
-    u32x4_t vst[V_ITEMS][2];
-    auto load = [&](int tile) {
-        const int soff = tile * KT * D * 2;
+    // Load x of wave w fills slots x * NTHR + 64 w + lane of a tile (the
+    // hardware places lane i's 16 bytes at the wave's LDS base + 16 i), so each
+    // lane fetches the global piece that the swizzle puts at its slot.
+    int dma_off[DMA_N];
 #pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            const int pi = tid + NTHR * i;
-            const int key = pi / PPR, c = pi % PPR;
-            kst[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (key * D + 8 * c) * 2, soff, 0);
-        }
+    for (int x = 0; x < DMA_N; ++x) {
+        const int slot = x * NTHR + wave * 64 + lane;
+        const int r = slot / PPR, c = (slot % PPR) ^ (r & (PPR - 1));
+        dma_off[x] = r * ROW_B + c * 16;
+    }
+    const uint32_t lds_base = (uint32_t)(size_t)(lds_void_t*)smem;
+    auto load = [&](int tile, int buf) {
+        const int soff = tile * TILE_B;
 #pragma unroll
-        for (int i = 0; i < V_ITEMS; ++i) {
-            const int it = tid + NTHR * i;
-            const int kp = it % (KT / 2), c = it / (KT / 2);
-            vst[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rv, (2 * kp * D + 8 * c) * 2, soff, 0);
-            vst[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * kp + 1) * D + 8 * c) * 2, soff, 0);
-        }
-    };
-    auto store = [&]() {
-#pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            const int pi = tid + NTHR * i;
-            s_k[kpos<PPR>(pi / PPR, pi % PPR)] = __builtin_bit_cast(uint4, kst[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < V_ITEMS; ++i) {
-            const int it = tid + NTHR * i;
-            const int kp = it % (KT / 2), c = it / (KT / 2);
-            const uint32_t a[4] = {vst[i][0].x, vst[i][0].y, vst[i][0].z, vst[i][0].w};
-            const uint32_t bq[4] = {vst[i][1].x, vst[i][1].y, vst[i][1].z, vst[i][1].w};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                // dims 8c+2x and 8c+2x+1, keys 2kp and 2kp+1
-                const uint32_t lo = (a[x] & 0xffffu) | (bq[x] << 16);
-                const uint32_t hi = (a[x] >> 16) | (bq[x] & 0xffff0000u);
-                const int d0 = 8 * c + 2 * x;
-                const int unit = kp >> 1, sub = (kp & 1) * 4;
-                *reinterpret_cast<uint32_t*>(s_vt + vt_byte(d0, unit) + sub) = lo;
-                *reinterpret_cast<uint32_t*>(s_vt + vt_byte(d0 + 1, unit) + sub) = hi;
-            }
+        for (int x = 0; x < DMA_N; ++x) {
+            const uint32_t dst = lds_base + (uint32_t)((x * NTHR + wave * 64) * 16);
+            load_lds16(rk, dst + (uint32_t)(buf * TILE_B), dma_off[x], soff);
+            load_lds16(rv, dst + (uint32_t)((2 + buf) * TILE_B), dma_off[x], soff);
         }
     };
+    // S operand: lane reads key row 16 mb + l16, piece 4 ks + lq.
+    int k_rd[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_rd[ks] = l16 * ROW_B + (((4 * ks + lq) ^ (l16 & (PPR - 1))) << 4);
+    // V^T operand, one transposed read per 4 keys: lanes 4i..4i+3 of each
+    // 16-lane group name key row i of the group (4 dims each) and lane n of the
+    // group receives dim n of all four rows.  Lane 16G + 4i + q names row
+    // 4G + i (+ 16 h + 32 kb) and dims 16 db + 4q .. 16 db + 4q + 3, so it gets
+    // keys 4G + 0..3 of dim 16 db + (lane mod 16): the key order of the
+    // weights that the score layout leaves in its registers.
+    const int vr = lane >> 2, vq = lane & 3;
+    int v_rd[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        v_rd[db] = vr * ROW_B + (((2 * db + (vq >> 1)) ^ (vr & (PPR - 1))) << 4) + ((vq & 1) << 3);
 
     f32x4_t oacc[DB][2];
 #pragma unroll
@@ -170,13 +180,18 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
     auto tile_of = [&](int it) { return it < nst ? it : wt0 + (it - nst); };
-    load(tile_of(0));
+    load(tile_of(0), 0);
     for (int it = 0; it < n_iter; ++it) {
         const int tile = tile_of(it);
+        const int buf = it & 1;
+        // this wave's loads of the tile are done; after the barrier every
+        // wave's are, and every wave has finished the previous tile, whose
+        // buffers the next loads overwrite
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        store();
-        __syncthreads();
-        if (it + 1 < n_iter) load(tile_of(it + 1));
+        if (it + 1 < n_iter) load(tile_of(it + 1), buf ^ 1);
+        const unsigned char* ktile = smem + buf * TILE_B;
+        const unsigned char* vtile = smem + (2 + buf) * TILE_B;
 
         // ---- S^T = K Q^T for 64 keys x 32 query rows
         f32x4_t sacc[4][2];
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
             for (int nb = 0; nb < 2; ++nb) sacc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s_k[kpos<PPR>(16 * mb + l16, 4 * ks + lq)]);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktile + k_rd[ks] + 16 * mb * ROW_B);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     sacc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[nb][ks], sacc[mb][nb], 0, 0, 0);
@@ -267,10 +282,11 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
                 for (int nb = 0; nb < 2; ++nb) bop[hl][nb] = __builtin_bit_cast(bf16x8_t, pk[hl][kb][nb]);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int dim = 16 * db + l16;
-                const uint2 u0 = *reinterpret_cast<const uint2*>(s_vt + vt_byte(dim, 8 * kb + lq));
-                const uint2 u1 = *reinterpret_cast<const uint2*>(s_vt + vt_byte(dim, 8 * kb + 4 + lq));
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+                const i16x4_t u0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t*)(vtile + v_rd[db] + 32 * kb * ROW_B));
+                const i16x4_t u1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t*)(vtile + v_rd[db] + (32 * kb + 16) * ROW_B));
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
                     oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[0][nb], oacc[db][nb], 0, 0, 0);
