@@ -76,9 +76,33 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int g = n_q / n_kv;
-    const int tq_idx = n_tq - 1 - (int)(blockIdx.x % n_tq);  // longest rows first
-    const int hc = blockIdx.x / n_tq;
-    const int j = blockIdx.y, b = blockIdx.z;
+    // Work item of this workgroup: query tile tq_idx of group (b, j, hc).
+    // Workgroups are dealt to the 8 XCDs round-robin by linear id, and when
+    // the grid is two workgroups per CU, the CU pairs ids L and L + N/2, the
+    // first of which wins most issue cycles.  Where the sizes allow, the map
+    // therefore (a) keeps every group's query tiles on one XCD, so its K/V
+    // tiles are reused from that XCD's L2, and (b) gives the ids of the first
+    // half the tiles longest first and those of the second half shortest
+    // first, so the two workgroups sharing a CU hold complementary amounts of
+    // work.  Otherwise it falls back to longest first within each group.
+    const int n_hc = gridDim.x / n_tq;
+    const int n_groups = n_hc * (int)gridDim.y * (int)gridDim.z;
+    const int n_wg = n_tq * n_groups;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    int tq_idx, grp;
+    if (n_groups % 16 == 0) {
+        const int half = n_wg / 2;                 // a multiple of 8 n_tq
+        const int hi = lin >= half, lh = lin - hi * half;
+        const int xcd = lh & 7, k = lh >> 3;       // k-th workgroup of this half on this XCD
+        const int per_xcd = n_groups / 16;         // groups per XCD and half
+        grp = hi * (n_groups / 2) + xcd * per_xcd + k / n_tq;
+        tq_idx = hi ? k % n_tq : n_tq - 1 - k % n_tq;
+    } else {
+        tq_idx = n_tq - 1 - (int)(blockIdx.x % n_tq);  // longest rows first
+        grp = blockIdx.x / n_tq + n_hc * (blockIdx.y + gridDim.y * blockIdx.z);
+    }
+    const int hc = grp % n_hc;
+    const int j = (grp / n_hc) % (int)gridDim.y, b = grp / (n_hc * (int)gridDim.y);
     int P = past_len[b];
     if (P < 0 || P > pmax) return;  // caller error: nothing is written for this sequence
     const int t0 = tq_idx * tq;
