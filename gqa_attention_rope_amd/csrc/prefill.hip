@@ -214,6 +214,17 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (it + 1 < n_iter) load(tile_of(it + 1), buf ^ 1);
+        // Issue priority grows with the tiles left: of two workgroups sharing
+        // a CU the one with more work left is served first, so both tend to
+        // finish together instead of the second running alone (one wave per
+        // SIMD) at the end.
+        {
+            const int rem = n_iter - it;
+            if (rem > 12) __builtin_amdgcn_s_setprio(3);
+            else if (rem > 8) __builtin_amdgcn_s_setprio(2);
+            else if (rem > 4) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         const unsigned char* ktile = smem + buf * TILE_B;
         const unsigned char* vtile = smem + (2 + buf) * TILE_B;
 
@@ -257,10 +268,18 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         for (int nb = 0; nb < 2; ++nb) {
             float mx = -INFINITY;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) mx = fmaxf(mx, fmaxf(fmaxf(sacc[mb][nb][0], sacc[mb][nb][1]),
-                                                              fmaxf(sacc[mb][nb][2], sacc[mb][nb][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            // v_maximum3 needs no canonicalising of its inputs (fmaxf does)
+            for (int mb = 0; mb < 4; ++mb)
+                mx = __builtin_elementwise_maximum(
+                    mx, __builtin_elementwise_maximum(
+                            __builtin_elementwise_maximum(sacc[mb][nb][0], sacc[mb][nb][1]),
+                            __builtin_elementwise_maximum(sacc[mb][nb][2], sacc[mb][nb][3])));
+            // lanes l, l ^ 16, l ^ 32 and l ^ 48 hold the same query row: two
+            // in-register lane swaps instead of LDS permutes
+            const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = __builtin_elementwise_maximum(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+            const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = __builtin_elementwise_maximum(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
             // The exponent reference m_ref (scaled, base 2) only moves when the row
             // maximum exceeds it by more than 8: weights then stay below 2^8, and
             // the accumulators are rescaled rarely instead of on every tile.
