@@ -346,6 +346,9 @@ PREFILL_CASES = [
     (2, 4, 4, 65, 128, 200, [0, 64], 5.0e5, "half", None),           # g = 1
     (1, 32, 2, 40, 128, 100, [27], 5.0e5, "interleaved", SCALED),    # g = 16
     (3, 16, 2, 1, 128, 300, [299 - 1, 10, 200], 5.0e5, "interleaved", None),  # T = 1
+    # 16 (sequence, KV head) groups: the XCD-local work map with complementary query tiles, ragged lengths
+    (2, 32, 8, 45, 128, 300, [17, 250], 5.0e5, "interleaved", None),
+    (2, 16, 8, 70, 64, 200, [5, 120], 1.0e4, "half", None),          # g = 2, d 64: two query tiles per group
 ]
 
 
