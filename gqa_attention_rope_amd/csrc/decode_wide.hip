@@ -174,10 +174,15 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
                 const int row = at * WD_TILE + rg * ROWS_W + 16 * k + 4 * lq + e;
                 const bool vis = row < L && (row >= geo.w0 || row < n_sink);
                 sacc[k][e] = vis ? sacc[k][e] * scale_log2 : -INFINITY;
-                tm = fmaxf(tm, sacc[k][e]);
+                tm = __builtin_elementwise_maximum(tm, sacc[k][e]);  // v_maximum3: no input canonicalising
             }
-        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        {
+            // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same head: in-register lane swaps, not LDS permutes
+            const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+            tm = __builtin_elementwise_maximum(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+            const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm), __float_as_uint(tm), false, false);
+            tm = __builtin_elementwise_maximum(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+        }
         const float mn = fmaxf(m_run, tm);
         const float mref = mn == -INFINITY ? 0.f : mn;
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run - mn);
