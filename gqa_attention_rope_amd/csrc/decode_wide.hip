@@ -149,6 +149,16 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
             }
         }
         if (i + 1 < t1) load_tile(i + 1);
+        // Issue priority grows with the tiles left, so that of two workgroups
+        // sharing a CU the one with more work is served first and the two
+        // tend to finish together (ragged contexts make the splits unequal).
+        {
+            const int rem = t1 - i;
+            if (rem > 12) __builtin_amdgcn_s_setprio(3);
+            else if (rem > 8) __builtin_amdgcn_s_setprio(2);
+            else if (rem > 4) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         __syncthreads();
 
         // scores of this wave's rows for its 16 heads
