@@ -20,18 +20,19 @@
 //    sink and window tiles only, under a window) are cut into nsplit
 //    contiguous ranges.  Wave w owns head block hb = w % HB (16 heads) and row
 //    group w / HB of each tile (RG = 4 / HB groups of 64 / RG rows).
-//  * A tile's K rows go to LDS row-major with an XOR swizzle (the MFMA A
-//    operand reads 16 rows of one 16-byte piece), V rows transposed (dim-major
-//    with a padded stride, so that the B operand's 4-row runs of one dim are
-//    8-byte reads on distinct banks).  One register stage prefetches the next
-//    tile while the current one is computed.
+//  * A tile's K and V rows go from HBM straight into LDS (range-checked
+//    buffer loads with the LDS destination), row-major with an XOR swizzle of
+//    the 16-byte pieces: the MFMA A operand reads of K (16 rows of one piece)
+//    and the transposed V reads (ds_read_b64_tr_b16, 16 rows of two pieces)
+//    both spread over all banks.  Double-buffered: the next tile's loads are
+//    in flight while the current one is computed, one barrier per tile.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A: 16 K rows x 32 dims; B: the
 //    wave's 16 rotated q rows, held in registers).  Lane l then holds rows
 //    4(l/16)+i of each 16-row block for head l%16: exactly the A operand of
 //    O += P V when the 32 rows of a K-step are taken in that order, so P never
 //    leaves the registers.  P enters as a bf16 high part plus a bf16
 //    remainder (two MFMAs, about 16 significant bits); V's B operand follows
-//    the same row order (two 8-byte reads per lane).
+//    the same row order (two transposed 8-byte reads per lane).
 //  * Online softmax per head (two lane shuffles per reduction); the output
 //    rescale fetches each head's factor from the lanes that own it.
 //  * Each (split, row group) writes one (max, sum, unnormalised output)
@@ -45,6 +46,7 @@
 #include "attn_window.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_direct.hpp"
 
 namespace gqa {
 
@@ -54,7 +56,6 @@ constexpr int WD_THREADS = 256;
 constexpr int WD_TILE = 64;
 constexpr float WD_LOG2E = 1.4426950408889634f;
 constexpr uint32_t WD_RSRC = 0x00020000u;  // raw buffer, 32-bit dwords
-constexpr int WD_VS = 68;                  // transposed V tile: elements per dim (64 rows + pad)
 
 __device__ __forceinline__ float wd_wave_max(float v) {
 #pragma unroll
@@ -85,10 +86,10 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
     constexpr int REC = D + 4;
     constexpr int NREC = RG;                         // records per split and head
 
-    __shared__ __align__(16) unsigned char s_k[TILEB];
-    __shared__ __align__(16) uint16_t s_vt[D * WD_VS];
+    // K buffers 0 and 1, then V buffers 0 and 1
+    __shared__ __align__(16) unsigned char smem[4 * TILEB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int hb = wave % HB, rg = wave / HB;
     const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -107,16 +108,36 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
         __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + seg), (short)0, L * ROWB, WD_RSRC);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + seg), (short)0, L * ROWB, WD_RSRC);
-    u32x4_t kb[HALF], vb[HALF];
-    auto load_tile = [&](int i) {
-        const int base = abs_tile(i) * TILEB + tid * 16;
+    // Load x of wave w fills slots x * 256 + 64 w + lane of a tile (lane i's 16
+    // bytes land at the wave's LDS base + 16 i), so each lane fetches the
+    // global piece that the swizzle puts at its slot: piece c of row r sits
+    // at slot r * PPR + (c ^ (r mod PPR)).
+    int dma_off[HALF];
+#pragma unroll
+    for (int x = 0; x < HALF; ++x) {
+        const int slot = x * WD_THREADS + wave * 64 + lane;
+        const int r = slot / PPR, c = (slot % PPR) ^ (r & (PPR - 1));
+        dma_off[x] = r * ROWB + c * 16;
+    }
+    const uint32_t lds_base = lds_addr(smem);
+    auto load_tile = [&](int i, int buf) {
+        const int soff = abs_tile(i) * TILEB;
 #pragma unroll
         for (int x = 0; x < HALF; ++x) {
-            kb[x] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + x * WD_THREADS * 16, 0, 0);
-            vb[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + x * WD_THREADS * 16, 0, 0);
+            const uint32_t dst = lds_base + (uint32_t)((x * WD_THREADS + wave * 64) * 16);
+            load_lds16(rk, dst + (uint32_t)(buf * TILEB), dma_off[x], soff);
+            load_lds16(rv, dst + (uint32_t)((2 + buf) * TILEB), dma_off[x], soff);
         }
     };
-    if (t0 < t1) load_tile(t0);
+    if (t0 < t1) load_tile(t0, 0);
+    // V operand reads: lane 16G + 4i + q names row 4G + i (+ the 16-row offset
+    // of the read) and dims 16 db + 4q .. + 3, and receives rows 4G + 0..3 of
+    // dim 16 db + (lane mod 16): the row order of the weights' registers.
+    const int vr = lane >> 2, vq = lane & 3;
+    int v_rd[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        v_rd[db] = vr * ROWB + (((2 * db + (vq >> 1)) ^ (vr & (PPR - 1))) << 4) + ((vq & 1) << 3);
 
     // B operand of the scores: 8 dims of head 16 hb + l16 per k-step (zero beyond g)
     const int hq = 16 * hb + l16;
@@ -135,20 +156,15 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
 
     for (int i = t0; i < t1; ++i) {
         const int at = abs_tile(i);
-        __syncthreads();  // the previous tile is consumed
-#pragma unroll
-        for (int x = 0; x < HALF; ++x) {
-            const int byte = tid * 16 + x * WD_THREADS * 16;
-            const int row = byte / ROWB, pc = (byte % ROWB) / 16;
-            *reinterpret_cast<u32x4_t*>(s_k + row * ROWB + 16 * (pc ^ (row & (PPR - 1)))) = kb[x];
-            const uint32_t w4[4] = {vb[x][0], vb[x][1], vb[x][2], vb[x][3]};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s_vt[(8 * pc + 2 * e) * WD_VS + row] = (uint16_t)(w4[e] & 0xffffu);
-                s_vt[(8 * pc + 2 * e + 1) * WD_VS + row] = (uint16_t)(w4[e] >> 16);
-            }
-        }
-        if (i + 1 < t1) load_tile(i + 1);
+        const int buf = (i - t0) & 1;
+        // this wave's loads of the tile are done; after the barrier every
+        // wave's are, and every wave has finished the previous tile, whose
+        // buffers the next loads overwrite
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (i + 1 < t1) load_tile(i + 1, buf ^ 1);
+        const unsigned char* s_k = smem + buf * TILEB;
+        const unsigned char* s_v = smem + (2 + buf) * TILEB;
         // Issue priority grows with the tiles left, so that of two workgroups
         // sharing a CU the one with more work is served first and the two
         // tend to finish together (ragged contexts make the splits unequal).
@@ -159,7 +175,6 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
             else if (rem > 4) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
         }
-        __syncthreads();
 
         // scores of this wave's rows for its 16 heads
         f32x4_t sacc[KB];
@@ -228,10 +243,9 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
             const int r0 = rg * ROWS_W + 32 * kk + 4 * lq;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const uint16_t* vcol = s_vt + (16 * db + l16) * WD_VS;
-                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vcol + r0);
-                const u32x2_t c = *reinterpret_cast<const u32x2_t*>(vcol + r0 + 16);
-                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], c[0], c[1]});
+                const i16x4_t a = read_tr16(s_v + v_rd[db] + (r0 - 4 * lq) * ROWB);
+                const i16x4_t c = read_tr16(s_v + v_rd[db] + (r0 - 4 * lq + 16) * ROWB);
+                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), bop, oacc[db], 0,
                                                                     0, 0);
                 oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), bop, oacc[db], 0,

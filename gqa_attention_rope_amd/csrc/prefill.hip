@@ -26,6 +26,7 @@
 // tiles that straddle a bound are masked element-wise.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_direct.hpp"
 
 namespace gqa {
 
@@ -35,21 +36,6 @@ constexpr int KT = 64;        // keys per tile
 constexpr int NTHR = 256;     // 4 waves
 constexpr int ROWS = 128;     // query rows per workgroup (32 per wave)
 constexpr float LOG2E_P = 1.4426950408889634f;
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-// A range-checked 16-byte-per-lane buffer load whose data goes to LDS (lane i
-// writes m0 + 16 i; lanes past the range write zeros).  Issued as inline asm:
-// through the builtin the compiler guards the later transposed LDS reads of
-// the other buffer with a wait for these loads, which would expose their
-// latency every tile.  The kernel waits for them itself (vmcnt(0) before the
-// barrier that publishes the tile).  The instruction has no register result.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voff, int soff) {
-    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
-                 : "memory");
-}
 
 // LDS tiles ([64 keys][D] bf16, row-major) are kept in 16-byte pieces; piece c
 // of key row r sits at slot c ^ (r mod PPR).  With this swizzle the K operand
@@ -170,7 +156,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         const int r = slot / PPR, c = (slot % PPR) ^ (r & (PPR - 1));
         dma_off[x] = r * ROW_B + c * 16;
     }
-    const uint32_t lds_base = (uint32_t)(size_t)(lds_void_t*)smem;
+    const uint32_t lds_base = lds_addr(smem);
     auto load = [&](int tile, int buf) {
         const int soff = tile * TILE_B;
 #pragma unroll
@@ -325,10 +311,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
                 for (int nb = 0; nb < 2; ++nb) bop[hl][nb] = __builtin_bit_cast(bf16x8_t, pk[hl][kb][nb]);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const i16x4_t u0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t*)(vtile + v_rd[db] + 32 * kb * ROW_B));
-                const i16x4_t u1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t*)(vtile + v_rd[db] + (32 * kb + 16) * ROW_B));
+                const i16x4_t u0 = read_tr16(vtile + v_rd[db] + 32 * kb * ROW_B);
+                const i16x4_t u1 = read_tr16(vtile + v_rd[db] + (32 * kb + 16) * ROW_B);
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
