@@ -55,16 +55,26 @@ constexpr int ST_TILE = 64;
 constexpr float ST_LOG2E = 1.4426950408889634f;
 constexpr uint32_t ST_RSRC = 0x00020000u;  // raw buffer, 32-bit dwords
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+// Wave-wide max and sum with every lane receiving the result, in registers:
+// DPP inside each row of 16 (quad_perm [1,0,3,2], [2,3,0,1], then row_ror:4
+// and row_ror:8, which bring in the other three quads of the row), then the
+// rows paired with v_permlane16_swap and v_permlane32_swap.  No LDS permutes.
+// The sum is associated differently in different lanes; each lane's order is
+// fixed, so every lane's result is reproducible.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+    auto op = [](float a, float b) { return MAX ? __builtin_elementwise_maximum(a, b) : a + b; };
+    v = op(v, dpp_f32<0xB1>(v));
+    v = op(v, dpp_f32<0x4E>(v));
+    v = op(v, dpp_f32<0x124>(v));
+    v = op(v, dpp_f32<0x128>(v));
+    const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v); }
 
 // D head size, HPW most heads one wave handles (g <= 4 * HPW)
 template <int D, int HPW>
