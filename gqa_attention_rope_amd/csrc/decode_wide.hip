@@ -57,16 +57,26 @@ constexpr int WD_TILE = 64;
 constexpr float WD_LOG2E = 1.4426950408889634f;
 constexpr uint32_t WD_RSRC = 0x00020000u;  // raw buffer, 32-bit dwords
 
-__device__ __forceinline__ float wd_wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+// Wave-wide max and sum in registers: DPP inside each row of 16 (quad_perm
+// [1,0,3,2], [2,3,0,1], row_ror:4, row_ror:8), then the rows paired with
+// v_permlane16_swap and v_permlane32_swap; no LDS permutes.  The sum's
+// association differs between lanes, so it is returned as lane 0's value:
+// every lane then uses the same, reproducible total.
+template <bool MAX>
+__device__ __forceinline__ float wd_wave_reduce(float v) {
+    auto op = [](float a, float b) { return MAX ? __builtin_elementwise_maximum(a, b) : a + b; };
+    v = op(v, dpp_f32<0xB1>(v));
+    v = op(v, dpp_f32<0x4E>(v));
+    v = op(v, dpp_f32<0x124>(v));
+    v = op(v, dpp_f32<0x128>(v));
+    const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
-__device__ __forceinline__ float wd_wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
+__device__ __forceinline__ float wd_wave_max(float v) { return wd_wave_reduce<true>(v); }
+__device__ __forceinline__ float wd_wave_sum(float v) { return wd_wave_reduce<false>(v); }
 
 // D head size; HB blocks of 16 heads (g <= 16 HB), HB in {2, 4}
 template <int D, int HB>
