@@ -5,9 +5,8 @@ anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may use it.  It shares no code, constants
 or helpers with the HIP library in ``gqa_attention_rope_amd/``.
 
-Parity status of each function is stated in its docstring; the functions
-whose values no page fixes (the blend band of Llama-3 scaled RoPE and the ramp
-of YaRN) say "parity unpinned".
+Parity status of each function is stated in the module docstring of
+``gqa_oracle``: every function is pinned to something other than itself.
 """
 
 from .gqa_oracle import (  # noqa: F401

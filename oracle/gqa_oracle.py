@@ -22,18 +22,20 @@ Tensor conventions (all bf16 tensors are numpy uint16 bit patterns):
 Parity status:
   bf16_to_f64 / f64_to_bf16   pinned (exact bit patterns, torch RNE, ties)
   rope_frequencies            pinned (closed form, geometric ratio)
-  llama3_scaled_frequencies   PARITY UNPINNED in the blend band: the pages name
-                              the factor and the two cutoffs but print no
-                              formula.  Only its limits are pinned (factor 1 is
-                              the identity, short wavelengths untouched,
-                              longest ones divided by the factor, continuity).
+  llama3_scaled_frequencies   pinned, blend band included: the pages name the
+                              factor and the two cutoffs but print no formula;
+                              the table matches an independently written
+                              library initialiser (transformers' Llama-3 rule)
+                              to fp32 rounding; limits and continuity too
   rope_frequencies linear     pinned (PI = plain RoPE at position p / s)
   rope_frequencies ntk        pinned (freq_0 = 1, lowest frequency divided by
                               exactly s, geometric progression)
-  yarn_frequencies            PARITY UNPINNED in the ramp (the pages only name
-                              YaRN); pinned: both limits, continuity, and it
-                              agrees with the separately written Llama-3 rule
-                              when given the same cutoffs
+  yarn_frequencies            pinned: the paper's ramp (linear in turns rho)
+                              against transformers' YaRN table (linear in
+                              ln rho): equal outside the ramp, the same band,
+                              and inside it the paper's ramp at the rho the
+                              library's ramp implies; limits, continuity, and
+                              agreement with the Llama-3 rule at equal cutoffs
   rope_attention_factor       pinned (closed form 0.1 ln s + 1; equal-position
                               q.k scales by its square)
   rotate_pairs / rope_append  pinned (complex multiplication, p = 0 identity,
@@ -165,7 +167,7 @@ def rope_frequencies(theta, d, scaling=None, rotary_dim=None):
 
 
 def llama3_scaled_frequencies(freq, factor, low_freq_factor, high_freq_factor, original_max_pos):
-    """Llama-3 frequency-dependent RoPE scaling.  PARITY UNPINNED in the blend.
+    """Llama-3 frequency-dependent RoPE scaling.
 
     Reading taken (the pages only name the fields): with wavelength
     lambda = 2 pi / freq, wavelengths shorter than original_max_pos /
@@ -175,7 +177,9 @@ def llama3_scaled_frequencies(freq, factor, low_freq_factor, high_freq_factor, o
     s = (original_max_pos / lambda - low_freq_factor) /
         (high_freq_factor - low_freq_factor).
     s is 1 at the short cutoff and 0 at the long one, so the rule is
-    continuous.
+    continuous.  Pinned, blend band included, against the frequency table of
+    an independently written library initialiser (Hugging Face transformers'
+    Llama-3 rule), to fp32 rounding.
     """
     freq = np.asarray(freq, dtype=np.float64)
     out = np.empty_like(freq)
@@ -194,7 +198,7 @@ def llama3_scaled_frequencies(freq, factor, low_freq_factor, high_freq_factor, o
 
 
 def yarn_frequencies(freq, factor, alpha, beta, original_max_pos):
-    """YaRN's "NTK-by-parts" frequencies.  PARITY UNPINNED in the ramp.
+    """YaRN's "NTK-by-parts" frequencies.
 
     Following the YaRN paper's definition (the pages cite the paper and name
     the method, nothing more): rho = original_max_pos / lambda counts the
@@ -203,6 +207,13 @@ def yarn_frequencies(freq, factor, alpha, beta, original_max_pos):
     the new frequency is (1 - gamma) freq / factor + gamma freq, so pairs that
     turn many times keep their frequency and pairs that turn less than alpha
     times are interpolated fully.
+
+    The paper's ramp is linear in rho.  The library implementations ramp
+    linearly in the pair index, i.e. in ln(rho), between the same two edges;
+    the oracle keeps the paper's.  Pinned against Hugging Face transformers'
+    YaRN table (untruncated edges): equal outside the ramp, the same ramp
+    band, and inside it the paper's gamma of the rho that the library's ramp
+    value implies.
     """
     freq = np.asarray(freq, dtype=np.float64)
     rho = original_max_pos * freq / (2.0 * math.pi)

@@ -52,6 +52,12 @@ MUTANTS = {
     "softmax not normalised": ("w = w / w.sum(axis=1, keepdims=True)", "w = w / w.sum(axis=1, keepdims=True).max()"),
     "value not written": ("vc[b][:, rows, :] = v_new[b]", "pass"),
     "key written unrotated": ("kc[b][:, rows, :] = k_rot", "kc[b][:, rows, :] = k_new[b]"),
+    "llama3 blend linear in wavelength": (
+        "s = (original_max_pos / wavelength - low_freq_factor) / (high_freq_factor - low_freq_factor)",
+        "s = (long_cut - wavelength) / (long_cut - short_cut)"),
+    "llama3 blend weights swapped": ("out[i] = (1.0 - s) * f / factor + s * f", "out[i] = s * f / factor + (1.0 - s) * f"),
+    "yarn ramp linear in wavelength": ("gamma = np.clip((rho - alpha) / (beta - alpha), 0.0, 1.0)",
+                                       "gamma = np.clip((1.0 / alpha - 1.0 / rho) / (1.0 / alpha - 1.0 / beta), 0.0, 1.0)"),
     "ties away from zero": ("y[nz] = np.ldexp(np.rint(np.ldexp(x[nz], -q)), q)",
                             "y[nz] = np.ldexp(np.trunc(np.ldexp(x[nz], -q) + np.copysign(0.5, x[nz])), q)"),
 }
@@ -212,7 +218,52 @@ def pin_yarn(m):
     return ok and math.isclose(dot, (0.1 * math.log(16.0) + 1.0) ** 2 * (q @ k), rel_tol=1e-10)
 
 
-PINS = [pin_partial_rotary, pin_position_interpolation, pin_ntk_lowest_frequency, pin_yarn, pin_complex_rotation, pin_frequencies, pin_position_offset, pin_torch_cast, pin_sdpa, pin_bruteforce,
+try:
+    from transformers import LlamaConfig
+    from transformers import modeling_rope_utils as hf_rope
+except ImportError:  # the library pins below need it; the mutants only they catch are then skipped
+    hf_rope = None
+
+LIBRARY_MUTANTS = {"llama3 blend linear in wavelength", "llama3 blend weights swapped",
+                   "yarn ramp linear in wavelength"}
+
+
+def _hf_table(kind, fields):
+    ctx = int(fields["factor"] * fields["original_max_position_embeddings"])
+    cfg = LlamaConfig(hidden_size=512, num_attention_heads=4, num_key_value_heads=2, head_dim=128,
+                      max_position_embeddings=ctx, rope_parameters=dict(fields, rope_type=kind, rope_theta=5.0e5))
+    fn = hf_rope._compute_llama3_parameters if kind == "llama3" else hf_rope._compute_yarn_parameters
+    return fn(cfg, device="cpu")[0].double().numpy()
+
+
+def pin_llama3_library(m):
+    # Llama 3.1's scaling (8, 1, 4, 8192) at theta 5e5, d 128 against the library's table, blend band included
+    lib = _hf_table("llama3", {"factor": 8.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
+                               "original_max_position_embeddings": 8192})
+    ours = m.rope_frequencies(5.0e5, 128, dict(type="llama3", factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                                               original_max_pos=8192))
+    return float(np.max(np.abs(ours - lib) / lib)) <= 1e-6
+
+
+def pin_yarn_library(m):
+    # same band as the library's ramp; inside it, rho from the library's (log-linear) ramp gives the paper's gamma
+    lib = _hf_table("yarn", {"factor": 16.0, "beta_slow": 1.0, "beta_fast": 32.0,
+                             "original_max_position_embeddings": 4096, "truncate": False})
+    plain = 5.0e5 ** (-np.arange(64) / 64.0)
+    ours = m.rope_frequencies(5.0e5, 128, dict(type="yarn", factor=16.0, beta_slow=1.0, beta_fast=32.0,
+                                               original_max_pos=4096))
+    gl = (lib - plain / 16) / (plain - plain / 16)
+    go = (ours - plain / 16) / (plain - plain / 16)
+    band = (gl > 1e-5) & (gl < 1 - 1e-5)
+    same_band = np.array_equal(band, (go > 1e-5) & (go < 1 - 1e-5))
+    outside = float(np.max(np.abs(ours[~band] - lib[~band]) / lib[~band])) <= 1e-6
+    inside = np.allclose(go[band], (32.0 ** gl[band] - 1.0) / 31.0, rtol=0, atol=1e-5)
+    return same_band and outside and inside
+
+
+LIBRARY_PINS = [pin_llama3_library, pin_yarn_library] if hf_rope is not None else []
+
+PINS = LIBRARY_PINS + [pin_partial_rotary, pin_position_interpolation, pin_ntk_lowest_frequency, pin_yarn, pin_complex_rotation, pin_frequencies, pin_position_offset, pin_torch_cast, pin_sdpa, pin_bruteforce,
         pin_window_rows, pin_window_slice, pin_sink_closed_form]
 
 
@@ -224,6 +275,8 @@ def test_unmodified_oracle_passes_every_pin():
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
     old, new = MUTANTS[name]
+    if name in LIBRARY_MUTANTS and not LIBRARY_PINS:
+        pytest.skip("transformers is not importable: the library pins are unavailable")
     assert SRC.count(old) >= 1, f"mutation site for {name!r} not found"
     m = load(SRC.replace(old, new), "oracle_mutant")
     failed = []
