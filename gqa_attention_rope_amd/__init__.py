@@ -152,6 +152,15 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context under which the binding's temporaries are made: with an explicit stream they are
+    allocated (and zero-filled) on that stream, so the caching allocator orders their reuse after
+    the library's kernels and the kernels see the fill complete."""
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _bf16(t, name, shape=None):
     import torch
     if t.dtype != torch.bfloat16:
@@ -220,14 +229,15 @@ def gqa_rope_append(q, k_new, v_new, k_cache, v_cache, past_len, max_past_len, t
     _bf16(v_new, "v_new", (B, n_kv, T, d))
     _bf16(k_cache, "k_cache", (B, n_kv, S, d))
     _bf16(v_cache, "v_cache", (B, n_kv, S, d))
-    past_len = _past(past_len, B)
-    if q_rot is None:
-        q_rot = torch.empty_like(q)
-    _bf16(q_rot, "q_rot", (B, n_q, T, d))
     p = rope_params(theta, layout, scaling, rotary_dim)
-    _check(lib().gqa_rope_append(_ptr(q), _ptr(q_rot), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(past_len), int(max_past_len), B, n_q, n_kv, T, d, S, ctypes.byref(p),
-                                 _stream(stream)))
+    with _on(stream):
+        past_len = _past(past_len, B)
+        if q_rot is None:
+            q_rot = torch.empty_like(q)
+        _bf16(q_rot, "q_rot", (B, n_q, T, d))
+        _check(lib().gqa_rope_append(_ptr(q), _ptr(q_rot), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(past_len), int(max_past_len), B, n_q, n_kv, T, d, S,
+                                     ctypes.byref(p), _stream(stream)))
     return q_rot
 
 
@@ -266,19 +276,20 @@ def gqa_decode_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, w
     _bf16(q_rot, "q_rot")
     _bf16(k_cache, "k_cache", (B, n_kv, S, d))
     _bf16(v_cache, "v_cache", (B, n_kv, S, d))
-    past_len = _past(past_len, B)
-    if out is None:
-        out = torch.empty_like(q_rot)
-    _bf16(out, "out", (B, n_q, 1, d))
-    need = gqa_decode_workspace_bytes(B, n_q, n_kv, d, S)
-    if workspace is None:
-        # the scheduling header at the start must be zero before first use
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q_rot.device)
     opts, _keep = _opts(window, n_sink, sink_logits, n_q, q_rot.device)
-    _check(lib().gqa_decode_attn_ex(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
-                                    _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B,
-                                    n_q, n_kv, d, S, float(scale), ctypes.byref(opts) if opts else None,
-                                    _stream(stream)))
+    need = gqa_decode_workspace_bytes(B, n_q, n_kv, d, S)
+    with _on(stream):
+        past_len = _past(past_len, B)
+        if out is None:
+            out = torch.empty_like(q_rot)
+        _bf16(out, "out", (B, n_q, 1, d))
+        if workspace is None:
+            # the scheduling header at the start must be zero before first use
+            workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q_rot.device)
+        _check(lib().gqa_decode_attn_ex(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len),
+                                        int(max_past_len), _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), B, n_q, n_kv, d, S,
+                                        float(scale), ctypes.byref(opts) if opts else None, _stream(stream)))
     return out
 
 
@@ -292,14 +303,15 @@ def gqa_prefill_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, 
     _bf16(q_rot, "q_rot")
     _bf16(k_cache, "k_cache", (B, n_kv, S, d))
     _bf16(v_cache, "v_cache", (B, n_kv, S, d))
-    past_len = _past(past_len, B)
-    if out is None:
-        out = torch.empty_like(q_rot)
-    _bf16(out, "out", (B, n_q, T, d))
     opts, _keep = _opts(window, n_sink, sink_logits, n_q, q_rot.device)
-    _check(lib().gqa_prefill_attn_ex(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len), int(max_past_len),
-                                     _ptr(out), B, n_q, n_kv, T, d, S, float(scale),
-                                     ctypes.byref(opts) if opts else None, _stream(stream)))
+    with _on(stream):
+        past_len = _past(past_len, B)
+        if out is None:
+            out = torch.empty_like(q_rot)
+        _bf16(out, "out", (B, n_q, T, d))
+        _check(lib().gqa_prefill_attn_ex(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len),
+                                         int(max_past_len), _ptr(out), B, n_q, n_kv, T, d, S, float(scale),
+                                         ctypes.byref(opts) if opts else None, _stream(stream)))
     return out
 
 
@@ -323,22 +335,24 @@ def gqa_decode_step(q, k_new, v_new, k_cache, v_cache, past_len, max_past_len, t
     _bf16(v_new, "v_new", (B, n_kv, 1, d))
     _bf16(k_cache, "k_cache", (B, n_kv, S, d))
     _bf16(v_cache, "v_cache", (B, n_kv, S, d))
-    past_len = _past(past_len, B)
-    if out is None:
-        out = torch.empty_like(q)
-    _bf16(out, "out", (B, n_q, 1, d))
     if q_rot is not None:
         _bf16(q_rot, "q_rot", (B, n_q, 1, d))
     need = gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S)
-    if workspace is None:
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     p = rope_params(theta, layout, scaling, rotary_dim)
     opts, _keep = _opts(window, n_sink, sink_logits, n_q, q.device)
-    _check(lib().gqa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(past_len),
-                                 int(max_past_len), _ptr(out), _ptr(q_rot) if q_rot is not None else None,
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(), B, n_q, n_kv, d, S,
-                                 ctypes.byref(p), float(scale), ctypes.byref(opts) if opts else None,
-                                 _stream(stream)))
+    with _on(stream):
+        past_len = _past(past_len, B)
+        if out is None:
+            out = torch.empty_like(q)
+        _bf16(out, "out", (B, n_q, 1, d))
+        if workspace is None:
+            workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+        _check(lib().gqa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(past_len), int(max_past_len), _ptr(out),
+                                     _ptr(q_rot) if q_rot is not None else None, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), B, n_q, n_kv, d, S,
+                                     ctypes.byref(p), float(scale), ctypes.byref(opts) if opts else None,
+                                     _stream(stream)))
     return out
 
 

@@ -239,6 +239,22 @@ def test_decode_end_to_end(case):
     check_out(got, ref, "decode")
 
 
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}d{c[3]}P{max(c[5])}")
+def test_decode_oracle_rope_end_to_end(case):
+    """rope_append + decode_attn against the oracle doing its own RoPE and append: the reference never
+    sees a GPU value (the tiny 6/2-head and one-layer Llama-3.1-8B shapes are the first two cases)."""
+    B, n_q, n_kv, d, S, past, theta, layout, scaling = case
+    say(f"decode e2e, oracle RoPE {case[:6]}")
+    q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=150 + case[1])
+    q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling)
+    ref = attend(q_ref, kc_ref, vc_ref, past, n_kv)
+    kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
+    q_rot = gq.gqa_rope_append(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling)
+    out = gq.gqa_decode_attn(q_rot, kc_d, vc_d, pl, max(past))
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, "decode, oracle RoPE")
+
+
 @pytest.mark.parametrize("case", DECODE_CASES[:4], ids=lambda c: f"B{c[0]}q{c[1]}kv{c[2]}P{max(c[5])}")
 def test_decode_kernel_isolated(case):
     """Attention alone on synthetic already-rotated q and cache rows."""
@@ -433,6 +449,55 @@ def test_full_size_batched_decode_layer():
 def test_full_size_long_context_scaled_decode():
     """B=64, 64/8 heads, ragged 4096..8191, scaled RoPE: one of the 80 layer calls (sampled)."""
     full_size_decode("llama70b_shape_decode_scaled", sample_b=[0, 17, 63])
+
+
+def test_full_size_long_context_scaled_decode_80_calls():
+    """The 70B-shaped workload as the bench runs it: one cache pair (B=64, 64/8 heads, 2 GiB), 80
+    sequential rope_append + decode_attn calls with their own new q/k/v (the bench's per-call inputs),
+    each rewriting row past_len[b].  Calls 0 and 79 are compared with the oracle on sampled sequences;
+    the oracle's cache for call c is the initial cache with row past_len[b] appended by call c."""
+    name = "llama70b_shape_decode_scaled"
+    w = synth.WORKLOADS[name]
+    B, n_q, n_kv, d, S, layers = w["B"], w["n_q"], w["n_kv"], w["d"], w["S"], w["layers"]
+    past = synth.past_lengths(B, w["past"], w["seed"])
+    say(f"{name}: {layers} calls on one cache pair, B={B} max past {past.max()}")
+    kc = torch.empty((B, n_kv, S, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    synth.fill_normal_bf16_(kc, w["seed"] * 1000)
+    synth.fill_normal_bf16_(vc, w["seed"] * 1000 + 1)
+    synth.poison_beyond(kc, past, 1)
+    synth.poison_beyond(vc, past, 1)
+    q = synth.normal_bf16((layers, B, n_q, 1, d), w["seed"] + 11, DEV)
+    kn = synth.normal_bf16((layers, B, n_kv, 1, d), w["seed"] + 12, DEV)
+    vn = synth.normal_bf16((layers, B, n_kv, 1, d), w["seed"] + 13, DEV)
+    sb = np.array([0, 17, 63])
+    kc_s, vc_s = synth.bits(kc[sb]), synth.bits(vc[sb])
+    pl = past_dev(past)
+    maxp = int(past.max())
+    ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    q_rot = torch.empty((B, n_q, 1, d), dtype=torch.bfloat16, device=DEV)
+    outs = {}
+    for c in range(layers):
+        gq.gqa_rope_append(q[c], kn[c], vn[c], kc, vc, pl, maxp, w["theta"], "interleaved", w["scaling"],
+                           q_rot=q_rot)
+        out = gq.gqa_decode_attn(q_rot, kc, vc, pl, maxp, workspace=ws)
+        if c in (0, layers - 1):
+            outs[c] = synth.bits(out[sb])
+    torch.cuda.synchronize()
+    for c, got in outs.items():
+        q_ref, kc_ref, vc_ref = rope_append(synth.bits(q[c][sb]), synth.bits(kn[c][sb]), synth.bits(vn[c][sb]),
+                                            kc_s, vc_s, past[sb], w["theta"], "interleaved", w["scaling"])
+        check_out(got, attend(q_ref, kc_ref, vc_ref, past[sb], n_kv), f"{name} call {c}")
+        if c == layers - 1:  # the cache holds the last call's rows; every other row is as it started
+            for i, b in enumerate(sb):
+                p = int(past[b])
+                assert max_ulp(synth.bits(kc[b, :, p]), kc_ref[i, :, p]) <= 1
+                assert np.array_equal(synth.bits(vc[b, :, p]), vc_ref[i, :, p])
+                assert np.array_equal(synth.bits(kc[b, :, :p]), kc_s[i, :, :p])
+                assert np.array_equal(synth.bits(vc[b, :, :p]), vc_s[i, :, :p])
+    assert int(ws[:256].count_nonzero()) == 0
+    del kc, vc
+    torch.cuda.empty_cache()
 
 
 def test_full_size_chunked_prefill():
