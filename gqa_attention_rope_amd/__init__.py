@@ -20,6 +20,8 @@ GQA_ERR_HEAD_DIM = -3
 GQA_ERR_RANGE = -4
 GQA_ERR_WORKSPACE = -5
 GQA_ERR_HIP = -6
+GQA_ERR_SCRATCH = -7
+GQA_DECODE_NOALLOC_MAX_BYTES = 64 << 20
 
 GQA_ROPE_INTERLEAVED = 0
 GQA_ROPE_HALF = 1
@@ -32,6 +34,7 @@ EXPORTED = (
     "gqa_decode_workspace_bytes",
     "gqa_decode_attn",
     "gqa_decode_attn_ex",
+    "gqa_decode_attn_noalloc",
     "gqa_prefill_attn",
     "gqa_prefill_attn_ex",
     "gqa_decode_step_workspace_bytes",
@@ -97,6 +100,9 @@ def lib():
     L.gqa_decode_attn_ex.argtypes = [vp, vp, vp, vp, i32, vp, vp, sz, i32, i32, i32, i32, i32, f32,
                                      ctypes.POINTER(GqaAttnOpts), vp]
     L.gqa_decode_attn_ex.restype = i32
+    L.gqa_decode_attn_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, f32,
+                                          ctypes.POINTER(GqaAttnOpts), vp]
+    L.gqa_decode_attn_noalloc.restype = i32
     L.gqa_prefill_attn.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, vp]
     L.gqa_prefill_attn.restype = i32
     L.gqa_prefill_attn_ex.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
@@ -135,7 +141,8 @@ def _check(status):
     if status == GQA_OK:
         return
     msg = gqa_status_string(status)
-    if status in (GQA_ERR_INVALID_ARG, GQA_ERR_GROUP, GQA_ERR_HEAD_DIM, GQA_ERR_RANGE, GQA_ERR_WORKSPACE):
+    if status in (GQA_ERR_INVALID_ARG, GQA_ERR_GROUP, GQA_ERR_HEAD_DIM, GQA_ERR_RANGE, GQA_ERR_WORKSPACE,
+                  GQA_ERR_SCRATCH):
         raise ValueError(f"{msg} (status {status})")
     raise GqaError(status, msg)
 
@@ -290,6 +297,29 @@ def gqa_decode_attn(q_rot, k_cache, v_cache, past_len, max_past_len, out=None, w
                                         int(max_past_len), _ptr(out), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), B, n_q, n_kv, d, S,
                                         float(scale), ctypes.byref(opts) if opts else None, _stream(stream)))
+    return out
+
+
+def gqa_decode_attn_noalloc(q_rot, k_cache, v_cache, past_len, max_past_len, out, scale=0.0, stream=None,
+                            window=0, n_sink=0, sink_logits=None):
+    """gqa_decode_attn without a workspace: the library's fixed per-GPU scratch holds the split-K records.
+    ``out`` [B, n_q, 1, d] bf16 must be given (nothing is allocated); past_len must already be a contiguous
+    device int32 tensor.  Calls that may overlap in time on one GPU race."""
+    import torch
+    B, n_q, T, d = q_rot.shape
+    if T != 1:
+        raise ValueError("decode takes exactly one new token per sequence")
+    n_kv, S = k_cache.shape[1], k_cache.shape[2]
+    _bf16(q_rot, "q_rot")
+    _bf16(k_cache, "k_cache", (B, n_kv, S, d))
+    _bf16(v_cache, "v_cache", (B, n_kv, S, d))
+    _bf16(out, "out", (B, n_q, 1, d))
+    if past_len.dtype != torch.int32 or not past_len.is_cuda or past_len.numel() != B or not past_len.is_contiguous():
+        raise ValueError("past_len must be a contiguous device int32 tensor with B entries")
+    opts, _keep = _opts(window, n_sink, sink_logits, n_q, q_rot.device)
+    _check(lib().gqa_decode_attn_noalloc(_ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(past_len),
+                                         int(max_past_len), _ptr(out), B, n_q, n_kv, d, S, float(scale),
+                                         ctypes.byref(opts) if opts else None, _stream(stream)))
     return out
 
 

@@ -5,10 +5,17 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "gqa.h"
 #include "kernels.hpp"
+
+// Decode scratch of gqa_decode_attn_noalloc: one copy per GPU, allocated when
+// the code object is loaded and held until the process ends.  In host code
+// this name is only a stand-in for the symbol; the device address of each
+// GPU's copy comes from hipGetSymbolAddress (decode_scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[GQA_DECODE_NOALLOC_MAX_BYTES];
 
 namespace {
 
@@ -55,6 +62,38 @@ std::vector<EvPair> g_prof[gqa::K_KINDS];
 hipEvent_t g_pending[gqa::K_KINDS] = {};
 
 int g_decode_wg = 0;
+
+// ---- no-allocation decode: per-device address of `scratch` -----------------
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// Address of the current device's copy of `scratch`, looked up once per
+// device with that device current.
+int decode_scratch_ptr(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hip_status(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return hip_status(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GQA_OK;
+}
+
+// Zeroes the decode workspace header (the split-K ticket counter) at the start
+// of every no-allocation call: the scratch holds whatever the last call on
+// this GPU left, and a fill kernel (not a memset node) keeps the call
+// capturable.
+__global__ void clear_header_kernel(float* ws) {
+    if (threadIdx.x < gqa::DECODE_WS_HEADER_FLOATS) ws[threadIdx.x] = 0.f;
+}
 
 }  // namespace
 
@@ -198,6 +237,37 @@ int gqa_decode_attn(const void* q_rot, const void* k_cache, const void* v_cache,
                               n_q, n_kv, d, S, scale, nullptr, stream);
 }
 
+int gqa_decode_attn_noalloc(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                            int max_past_len, void* out, int B, int n_q, int n_kv, int d, int S, float scale,
+                            const gqa_attn_opts* opts, void* stream) {
+    if (!q_rot || !k_cache || !v_cache || !past_len || !out) return GQA_ERR_INVALID_ARG;
+    const gqa_attn_opts o = opts ? *opts : gqa_attn_opts{0, 0, nullptr};
+    if (o.window < 0 || o.n_sink < 0 || (o.sink_logits && (reinterpret_cast<uintptr_t>(o.sink_logits) & 3u)))
+        return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(past_len) & 3u))
+        return GQA_ERR_INVALID_ARG;
+    if (!(scale == scale) || isinf(scale)) return GQA_ERR_INVALID_ARG;
+    int st = check_shape(B, n_q, n_kv, 1, d, S, max_past_len);
+    if (st != GQA_OK) return st;
+    if (gqa::decode_launch_workspace_bytes(B, n_q, n_kv, d) > (size_t)GQA_DECODE_NOALLOC_MAX_BYTES)
+        return GQA_ERR_SCRATCH;
+    st = ensure_device();
+    if (st != GQA_OK) return st;
+    void* ws = nullptr;
+    st = decode_scratch_ptr(&ws);
+    if (st != GQA_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(64), 0, hs, static_cast<float*>(ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e);
+    e = gqa::launch_decode(static_cast<const uint16_t*>(q_rot), static_cast<const uint16_t*>(k_cache),
+                           static_cast<const uint16_t*>(v_cache), past_len, max_past_len,
+                           static_cast<uint16_t*>(out), static_cast<float*>(ws), B, n_q, n_kv, d, S,
+                           resolve_scale(scale, d), o.window, o.n_sink, o.sink_logits, g_decode_wg, hs);
+    return e == hipSuccess ? GQA_OK : hip_status(e);
+}
+
 size_t gqa_decode_step_workspace_bytes(int B, int n_q, int n_kv, int d, int S) {
     if (check_shape(B, n_q, n_kv, 1, d, S, 0) != GQA_OK) return 0;
     if (n_q / n_kv > GQA_DECODE_STEP_MAX_GROUP || B > 65535 || n_kv > 65535) return 0;
@@ -273,6 +343,9 @@ const char* gqa_status_string(int status) {
         case GQA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
         case GQA_ERR_RANGE: return "max_past_len must be >= 0 and max_past_len + T <= S";
         case GQA_ERR_WORKSPACE: return "workspace smaller than gqa_decode_workspace_bytes()";
+        case GQA_ERR_SCRATCH:
+            return "shape needs more decode scratch than the fixed no-allocation buffer holds "
+                   "(its split-K records exceed GQA_DECODE_NOALLOC_MAX_BYTES)";
         case GQA_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
         default: return "unknown status";
     }

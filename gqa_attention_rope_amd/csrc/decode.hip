@@ -945,25 +945,39 @@ DecodePlan decode_plan(int n_q, int n_kv, int d) {
     return p;
 }
 
-size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d) {
+namespace {
+int g_wide_min = DECODE_WIDE_MIN_G;
+
+// workspace of the split-K path, and of the wide-group path where it can take the shape
+size_t split_workspace_bytes(int B, int n_q, int n_kv, int d) {
     const DecodePlan p = decode_plan(n_q, n_kv, d);
     const int bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
     const size_t segs = (size_t)bs * n_kv * p.nhc;
     // static pieces: segment + workgroup < segs + G; chunk pieces: segs + G + chunk + segment
     const size_t slots = 2 * segs + DECODE_MAX_WG + DECODE_MAX_CHUNKS;
-    size_t need = (HDR_FLOATS + slots * p.slot_floats) * sizeof(float);
-    // the same workspace serves the wide-group kernel when it takes the shape
-    const int g = n_q / n_kv;
-    if (g <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS) {
-        const size_t wide = HDR_FLOATS * sizeof(float) + decode_wide_record_bytes(B, n_q, n_kv, d);
+    return (HDR_FLOATS + slots * p.slot_floats) * sizeof(float);
+}
+bool wide_eligible(int n_q, int n_kv) { return n_q / n_kv <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS; }
+size_t wide_workspace_bytes(int B, int n_q, int n_kv, int d) {
+    return HDR_FLOATS * sizeof(float) + decode_wide_record_bytes(B, n_q, n_kv, d);
+}
+bool takes_wide(int n_q, int n_kv) { return wide_eligible(n_q, n_kv) && n_q / n_kv >= g_wide_min; }
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d) {
+    size_t need = split_workspace_bytes(B, n_q, n_kv, d);
+    // the same workspace serves the wide-group kernel whenever it may take the
+    // shape (its threshold can be changed between calls)
+    if (wide_eligible(n_q, n_kv)) {
+        const size_t wide = wide_workspace_bytes(B, n_q, n_kv, d);
         if (wide > need) need = wide;
     }
     return need;
 }
 
-namespace {
-int g_wide_min = DECODE_WIDE_MIN_G;
-}  // namespace
+size_t decode_launch_workspace_bytes(int B, int n_q, int n_kv, int d) {
+    return takes_wide(n_q, n_kv) ? wide_workspace_bytes(B, n_q, n_kv, d) : split_workspace_bytes(B, n_q, n_kv, d);
+}
 
 void set_decode_wide_min_group(int g) { g_wide_min = g > 0 ? g : DECODE_WIDE_MIN_G; }
 int decode_wide_min_group() { return g_wide_min; }
@@ -972,7 +986,7 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
                          int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
                          int wg_override, hipStream_t st) {
-    if (n_q / n_kv >= g_wide_min && n_q / n_kv <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS)
+    if (takes_wide(n_q, n_kv))
         return launch_decode_wide(q_rot, k_cache, v_cache, past_len, max_past_len, out, ws, B, n_q, n_kv, d, S, scale,
                                   window, n_sink, sink_logits, wg_override, st);
     const DecodePlan p = decode_plan(n_q, n_kv, d);

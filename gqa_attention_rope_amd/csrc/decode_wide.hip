@@ -369,8 +369,13 @@ int decode_wide_splits(int nb, int n_kv, int g, int max_past_len, int window, in
 size_t decode_wide_record_bytes(int B, int n_q, int n_kv, int d) {
     int nb = DECODE_WIDE_MAX_SEGS / n_kv;
     if (nb > B) nb = B;
-    // at most WD_MAX_SEG_RECORDS records per segment
-    return (size_t)nb * n_kv * WD_MAX_SEG_RECORDS * (d + 4) * sizeof(float);
+    // records per segment: rg row groups x g heads per split, at most
+    // DECODE_WIDE_MAX_SPLITS splits and at most WD_MAX_SEG_RECORDS in all
+    const int g = n_q / n_kv;
+    const long long per_split = (long long)(g <= 32 ? 2 : 1) * g;
+    long long recs = per_split * DECODE_WIDE_MAX_SPLITS;
+    if (recs > WD_MAX_SEG_RECORDS) recs = WD_MAX_SEG_RECORDS;
+    return (size_t)nb * n_kv * (size_t)recs * (d + 4) * sizeof(float);
 }
 
 hipError_t launch_decode_wide(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,

@@ -66,6 +66,8 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int n_q, int n_kv, int d);
 size_t decode_workspace_bytes(int B, int n_q, int n_kv, int d);
+// the part of it that a launch with the current settings uses (split-K or wide-group records)
+size_t decode_launch_workspace_bytes(int B, int n_q, int n_kv, int d);
 void set_decode_schedule(int static_permille, int chunk_tiles);
 void set_decode_slot_ratio(int ratio_permille);  // 0: per-variant defaults
 int decode_slot_ratio();

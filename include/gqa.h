@@ -56,6 +56,7 @@ extern "C" {
 #define GQA_ERR_RANGE (-4)       /* max_past_len < 0, or max_past_len + T > S */
 #define GQA_ERR_WORKSPACE (-5)   /* workspace smaller than gqa_decode_workspace_bytes() */
 #define GQA_ERR_HIP (-6)         /* no device, launch or runtime failure; see gqa_status_string */
+#define GQA_ERR_SCRATCH (-7)     /* gqa_decode_attn_noalloc: the shape needs more than GQA_DECODE_NOALLOC_MAX_BYTES */
 
 /* ---- RoPE parameters ------------------------------------------------- */
 #define GQA_ROPE_INTERLEAVED 0 /* pair i is dims (2i, 2i+1) */
@@ -226,6 +227,33 @@ int gqa_decode_attn_ex(const void* q_rot, const void* k_cache, const void* v_cac
 int gqa_prefill_attn_ex(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
                         int max_past_len, void* out, int B, int n_q, int n_kv, int T, int d, int S, float scale,
                         const gqa_attn_opts* opts, void* stream);
+
+/*
+ * gqa_decode_attn_noalloc -- gqa_decode_attn_ex without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split-K records live in a fixed buffer inside the library, one copy per
+ * GPU of GQA_DECODE_NOALLOC_MAX_BYTES (64 MiB), reserved when the library is
+ * loaded and held until the process ends.  Same kernels, launch shape and
+ * results as gqa_decode_attn_ex (bitwise), plus one small kernel that clears
+ * the buffer's scheduling header first.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine).
+ *
+ * Every call on one GPU shares that GPU's buffer: calls that may overlap in
+ * time on one GPU (different streams without ordering, several host threads)
+ * race and give wrong results.  Order them on one stream.
+ *
+ * Arguments, layouts and ownership as gqa_decode_attn_ex.  Errors:
+ * INVALID_ARG, GROUP, HEAD_DIM, RANGE, SCRATCH (the records of the decode
+ * path the shape takes need more than GQA_DECODE_NOALLOC_MAX_BYTES: never
+ * for sizes where gqa_decode_workspace_bytes() is within it, e.g. B <= 256 at
+ * 32/8 heads or B <= 64 at 64/8, d 128; checked on the host, nothing
+ * launched), HIP.
+ */
+#define GQA_DECODE_NOALLOC_MAX_BYTES (64u << 20)
+int gqa_decode_attn_noalloc(const void* q_rot, const void* k_cache, const void* v_cache, const int32_t* past_len,
+                            int max_past_len, void* out, int B, int n_q, int n_kv, int d, int S, float scale,
+                            const gqa_attn_opts* opts, void* stream);
 
 /*
  * gqa_decode_step -- one decode step in a single launch, for small batches:

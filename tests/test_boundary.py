@@ -288,3 +288,38 @@ def test_wide_group_override():
     L = gq.lib()
     # the decode workspace also covers the wide-group kernel for MQA shapes
     assert L.gqa_decode_workspace_bytes(16, 64, 1, 128, 8192) >= 256 + 16 * 32 * 64 * 132 * 4
+
+
+# ---------------------------------------------------------------- no-allocation decode (host-side checks)
+
+def decode_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, pl=FAKE, maxp=10, out=FAKE, B=2, n_q=8, n_kv=2, d=128, S=64, scale=0.0)
+    a.update(kw)
+    return gq.lib().gqa_decode_attn_noalloc(P(a["q"]), P(a["kc"]), P(a["vc"]), P(a["pl"]), a["maxp"], P(a["out"]),
+                                            a["B"], a["n_q"], a["n_kv"], a["d"], a["S"], a["scale"], None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INV), (dict(out=0), INV), (dict(pl=FAKE + 2), INV), (dict(out=FAKE + 8), INV), (dict(B=0), INV),
+    (dict(scale=float("nan")), INV), (dict(n_q=6, n_kv=4), GRP), (dict(d=96), HD), (dict(maxp=64), RNG),
+    # 2048 sequences of 32/8 heads: 86.6 MiB of split-K records, beyond the fixed 64 MiB buffer
+    (dict(B=2048, n_q=32, n_kv=8, S=8192, maxp=100), gq.GQA_ERR_SCRATCH),
+])
+def test_decode_noalloc_rejects_on_host(kw, code):
+    assert decode_noalloc(**kw) == code
+    assert gq.gqa_status_string(code)
+
+
+def test_decode_noalloc_sizes_within_its_buffer():
+    # the headline and long-context shapes fit the fixed buffer; the check uses the path's own record bytes
+    assert gq.gqa_decode_workspace_bytes(32, 32, 8, 128, 8192) <= gq.GQA_DECODE_NOALLOC_MAX_BYTES
+    assert gq.gqa_decode_workspace_bytes(64, 64, 8, 128, 8192) <= gq.GQA_DECODE_NOALLOC_MAX_BYTES
+    assert "no-allocation" in gq.gqa_status_string(gq.GQA_ERR_SCRATCH)
+
+
+def test_decode_noalloc_without_device_is_a_hip_error():
+    # a valid call reaches the device lookup, which fails cleanly here (no GPU in this container)
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert decode_noalloc() == HIP
