@@ -41,6 +41,9 @@
 //    weights go through a small per-wave LDS buffer, and for the weighted
 //    value sum every lane owns d/64 output dims of all the wave's heads, so
 //    the accumulator is a few registers.
+//  * Before its first loads, each workgroup also writes the record directory
+//    entries of a few segments (where their records are and how many), so
+//    the merge needs neither past_len nor the share arithmetic.
 //  * A second kernel merges the records of each (sequence, head) in a fixed
 //    order: M = max m, l = sum l e^(m-M), o = sum o e^(m-M) / l, and clears
 //    the ticket counter for the next call.  Results are bitwise reproducible
@@ -213,9 +216,10 @@ __device__ __forceinline__ int kpos_byte(int R, int c) {
     return R * (D * 2) + ((c ^ (R & (PPR - 1))) << 4);
 }
 
-// Tile schedule shared by the partial and combine kernels: tiles [0, Ts) are
-// split into equal contiguous shares, tiles [Ts, T_all) into chunks of C.
-// Tile counts fit in 32 bits: at most 2048 sequences x n_q segments x S/64 tiles.
+// Tile schedule shared by the partial kernel and its record directory: tiles
+// [0, Ts) are split into contiguous shares, tiles [Ts, T_all) into chunks of
+// C.  Tile counts fit in 32 bits: at most 2048 sequences x n_q segments x
+// S/64 tiles.
 struct Sched {
     int T_all, Ts, n_dyn, C;
 };
@@ -242,8 +246,9 @@ constexpr int F_GRABBED = 8;    // this stage's atomic took a ticket
 template <int D, int HGW, int NHG>
 __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
-    const int32_t* __restrict__ past_len, int pmax, float* __restrict__ ws, int B, int n_q, int n_kv, int S, int nhc,
-    float scale_log2, int static_pm, int chunk, int window, int n_sink, Shares shares) {
+    const int32_t* __restrict__ past_len, int pmax, float* __restrict__ ws, int4* __restrict__ dir,
+    float* __restrict__ recs, int B, int n_q, int n_kv, int S, int nhc, float scale_log2, int static_pm, int chunk,
+    int window, int n_sink, Shares shares) {
     using C = Cfg<D, HGW, NHG>;
     constexpr int KB = C::KB, KS = C::KS;
     constexpr int DPL = D / 64;                  // value dims each lane accumulates
@@ -269,7 +274,6 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const int G = gridDim.x, w = blockIdx.x;
     const int dyn_slot0 = n_segs + G;  // slot of chunk t's piece in segment s: dyn_slot0 + t + s
     int* const ticket_ctr = reinterpret_cast<int*>(ws);
-    float* const recs = ws + HDR_FLOATS;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -357,6 +361,33 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         __syncthreads();
         take_ticket(uni(s_ticket));
         __syncthreads();
+    }
+
+    // Record directory for the combine: for segment s, the slot of its first
+    // static piece and their count, the slot of its first chunk piece and
+    // their count, the first static workgroup and the static tile total.
+    // Workgroup w fills the entries of segments w + G k (one per thread).  The
+    // stores go out before the first tile loads, so the waits for those loads
+    // keep their fixed counts.
+    for (int s = w + G * tid; s < n_segs; s += G * THREADS) {
+        const int b = s / segs_per_b, sj = s - b * segs_per_b;
+        const int nt = s_pre[b + 1] - s_pre[b];
+        const long long start = (long long)segs_per_b * s_pre[b] + (long long)sj * nt;
+        const long long end = start + nt;
+        const long long s_end = end < sc.Ts ? end : sc.Ts;
+        int w_lo = 0, n_st = 0;
+        if (start < s_end) {
+            w_lo = (int)owner_of(start, sc.Ts, shares);
+            n_st = (int)owner_of(s_end - 1, sc.Ts, shares) - w_lo + 1;
+        }
+        const long long d_start = start > sc.Ts ? start : sc.Ts;
+        int t_lo = 0, n_dy = 0;
+        if (d_start < end) {
+            t_lo = (int)((d_start - sc.Ts) / sc.C);
+            n_dy = (int)((end - 1 - sc.Ts) / sc.C) - t_lo + 1;
+        }
+        dir[2 * s] = make_int4(w_lo + s, n_st, dyn_slot0 + t_lo + s, n_dy);
+        dir[2 * s + 1] = make_int4(w_lo, sc.Ts, 0, 0);
     }
 
     // The q piece of a tile's segment, one 16-byte piece per thread (the
@@ -676,16 +707,18 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
 
 // Merge of the partial records of one (sequence, query head), in a fixed
 // order: the static shares that hold tiles of the head's segment, in
-// workgroup order, then its chunks in chunk order.  Four waves share the
-// records (wave k takes records k, k+4, ...), each merging its own online
-// (running max, rescaled sum and output) with all of its loads in flight
-// together; the four states then merge in wave order through LDS.  Block
-// (0, 0) also clears the ticket counter, so the next call starts from zero.
+// workgroup order, then its chunks in chunk order.  Where they are comes from
+// the directory the partial kernel wrote.  Four waves share the records
+// (wave k takes records k, k+4, ...), each merging its own online (running
+// max, rescaled sum and output) with all of its loads in flight together; the
+// four states then merge in wave order through LDS.  Block (0, 0) also clears
+// the ticket counter, so the next call starts from zero.
 constexpr int CMB_WAVES = 4;
 // The records of one segment, in merge order: the static shares of
-// workgroups w_lo .. w_lo + n_st - 1, then consecutive chunk records.
+// workgroups w_lo .. w_lo + n_st - 1 (slots st0 ..), then consecutive chunk
+// records (slots dy0 ..).
 struct RecordList {
-    int nrec, n_st, w_lo, seg, dyn0;  // dyn0: slot of the first chunk record, less seg
+    int nrec, n_st, w_lo, st0, dy0;
     long long Ts;
 };
 // Slot of record idx (record 0's for idx >= nrec) and whether it holds data:
@@ -696,18 +729,17 @@ __device__ __forceinline__ int record_slot(const RecordList rl, int idx, const S
     if (idx < rl.n_st) {
         const int w = rl.w_lo + idx;
         use = use && share_begin(w, rl.Ts, sh) < share_begin(w + 1, rl.Ts, sh);
-        return w + rl.seg;
+        return rl.st0 + idx;
     }
-    return rl.dyn0 + (idx - rl.n_st) + rl.seg;
+    return rl.dy0 + (idx - rl.n_st);
 }
 template <int D>
 __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* __restrict__ ws,
-                                                                        const int32_t* __restrict__ past_len,
-                                                                        int pmax, uint16_t* __restrict__ out, int B,
-                                                                        int n_q, int n_kv, int nhc, int gc, int G,
-                                                                        int static_pm, int chunk, int window,
-                                                                        int n_sink, const float* sink_logits,
-                                                                        Shares shares) {
+                                                                        const int4* __restrict__ dir,
+                                                                        const float* __restrict__ recs,
+                                                                        uint16_t* __restrict__ out, int n_q,
+                                                                        int n_kv, int nhc, int gc,
+                                                                        const float* sink_logits, Shares shares) {
     constexpr int DPL = D / 64;  // dims per lane
     constexpr int REC = D + 4;
     constexpr int RB = 8;        // records per wave and batch
@@ -717,53 +749,15 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = n_q / n_kv;
     if (h == 0 && b == 0 && tid == 0) reinterpret_cast<int*>(ws)[0] = 0;
-    const float* recs = ws + HDR_FLOATS;
     const size_t slot_floats = (size_t)gc * REC;
 
-    // prefix of tile counts (same clamping as the partial kernel)
-    long long pre_b = 0, total = 0;
-    for (int base = 0; base < B; base += 64) {
-        const int bb = base + lane;
-        const int n = bb < B ? tiles_of(past_len, bb, pmax, window, n_sink) : 0;
-        int before = (bb < b) ? n : 0;
-        int all = n;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            before += __shfl_xor(before, off, 64);
-            all += __shfl_xor(all, off, 64);
-        }
-        pre_b += before;
-        total += all;
-    }
-    const int nt_b = tiles_of(past_len, b, pmax, window, n_sink);
-
     const int j = h / g, hh = h % g, hc = hh / gc, hl = hh % gc;
-    const long long segs_per_b = (long long)n_kv * nhc;
-    const long long n_segs = (long long)B * segs_per_b;
-    const Sched sc = make_sched((int)(segs_per_b * total), static_pm, chunk);
-    const long long seg = (long long)b * segs_per_b + (long long)j * nhc + hc;
-    const long long start = segs_per_b * pre_b + (long long)(j * nhc + hc) * nt_b;
-    const long long end = start + nt_b;
-    // static shares: candidate workgroups w_lo..w_lo + n_st - 1 (some may hold no tile)
-    const long long s_end = end < sc.Ts ? end : sc.Ts;
-    long long w_lo = 0, n_st = 0;
-    if (start < s_end) {
-        w_lo = owner_of(start, sc.Ts, shares);
-        n_st = owner_of(s_end - 1, sc.Ts, shares) - w_lo + 1;
-    }
-    // chunks t_lo..t_lo + n_dy - 1
-    const long long d_start = start > sc.Ts ? start : sc.Ts;
-    long long t_lo = 0, n_dy = 0;
-    if (d_start < end) {
-        t_lo = (d_start - sc.Ts) / sc.C;
-        n_dy = (end - 1 - sc.Ts) / sc.C - t_lo + 1;
-    }
-    const int nrec = (int)(n_st + n_dy);
-    const long long dyn_slot0 = n_segs + G;
-
+    const int seg = (b * n_kv + j) * nhc + hc;
+    const int4 e0 = dir[2 * seg], e1 = dir[2 * seg + 1];
     // record idx is used if it exists and (static) its workgroup had a non-empty share;
     // record 0 always exists, so unused entries read it and are ignored
-    const RecordList rl{nrec, (int)n_st, (int)w_lo, (int)seg, (int)(dyn_slot0 + t_lo), sc.Ts};
+    const RecordList rl{e0.y + e0.w, e0.y, e1.x, e0.x, e0.z, e1.y};
+    const int nrec = rl.nrec;
 
     float M = -INFINITY, L = 0.f, acc[DPL];
 #pragma unroll
@@ -832,13 +826,13 @@ __global__ __launch_bounds__(64 * CMB_WAVES) void decode_combine_kernel(float* _
 
 template <int D, int HGW, int NHG>
 hipError_t launch_partial_t(int G, const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
-                            const int32_t* past_len, int pmax, float* ws, int B, int n_q, int n_kv, int S, int nhc,
-                            float scale_log2, int static_pm, int chunk, int window, int n_sink,
-                            const Shares& shares, hipStream_t st) {
+                            const int32_t* past_len, int pmax, float* ws, int4* dir, float* recs, int B, int n_q,
+                            int n_kv, int S, int nhc, float scale_log2, int static_pm, int chunk, int window,
+                            int n_sink, const Shares& shares, hipStream_t st) {
     const size_t dyn = (size_t)(B + 1) * sizeof(int);
     hipLaunchKernelGGL((decode_partial_kernel<D, HGW, NHG>), dim3(G), dim3(THREADS), dyn, st, q_rot, k_cache,
-                       v_cache, past_len, pmax, ws, B, n_q, n_kv, S, nhc, scale_log2, static_pm, chunk, window,
-                       n_sink, shares);
+                       v_cache, past_len, pmax, ws, dir, recs, B, n_q, n_kv, S, nhc, scale_log2, static_pm, chunk,
+                       window, n_sink, shares);
     return hipGetLastError();
 }
 
@@ -853,7 +847,8 @@ int occupancy_t(int B) {
 
 using occ_fn = int (*)(int);
 using partial_fn = hipError_t (*)(int, const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int, float*,
-                                  int, int, int, int, int, float, int, int, int, int, const Shares&, hipStream_t);
+                                  int4*, float*, int, int, int, int, int, float, int, int, int, int, const Shares&,
+                                  hipStream_t);
 
 struct Variant {
     int hgw, nhg;
@@ -928,6 +923,7 @@ void set_decode_schedule(int static_permille, int chunk_tiles) {
     g_chunk = chunk_tiles;
 }
 
+
 void set_decode_slot_ratio(int ratio_permille) { g_slot_ratio_pm = ratio_permille; }
 int decode_slot_ratio() { return g_slot_ratio_pm; }
 
@@ -949,13 +945,19 @@ namespace {
 int g_wide_min = DECODE_WIDE_MIN_G;
 
 // workspace of the split-K path, and of the wide-group path where it can take the shape
-size_t split_workspace_bytes(int B, int n_q, int n_kv, int d) {
+// Split-K workspace layout: the 256-byte header, the record directory (two
+// int4 per segment of one launch), then the records.
+size_t split_segments(int B, int n_q, int n_kv, int d) {
     const DecodePlan p = decode_plan(n_q, n_kv, d);
     const int bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
-    const size_t segs = (size_t)bs * n_kv * p.nhc;
+    return (size_t)bs * n_kv * p.nhc;
+}
+size_t split_workspace_bytes(int B, int n_q, int n_kv, int d) {
+    const DecodePlan p = decode_plan(n_q, n_kv, d);
+    const size_t segs = split_segments(B, n_q, n_kv, d);
     // static pieces: segment + workgroup < segs + G; chunk pieces: segs + G + chunk + segment
     const size_t slots = 2 * segs + DECODE_MAX_WG + DECODE_MAX_CHUNKS;
-    return (HDR_FLOATS + slots * p.slot_floats) * sizeof(float);
+    return (HDR_FLOATS + 8 * segs + slots * p.slot_floats) * sizeof(float);
 }
 bool wide_eligible(int n_q, int n_kv) { return n_q / n_kv <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS; }
 size_t wide_workspace_bytes(int B, int n_q, int n_kv, int d) {
@@ -1023,6 +1025,8 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
     const float scale_log2 = scale * LOG2E;
     const int spm = g_static_pm;
     const Shares shares = make_shares(G, cu_count, g_slot_ratio_pm > 0 ? g_slot_ratio_pm : default_slot_ratio(v));
+    int4* const dir = reinterpret_cast<int4*>(ws + HDR_FLOATS);
+    float* const recs = ws + HDR_FLOATS + 8 * split_segments(B, n_q, n_kv, d);
 
     for (int b0 = 0; b0 < B; b0 += DECODE_MAX_B) {
         const int nb = (B - b0) < DECODE_MAX_B ? (B - b0) : DECODE_MAX_B;
@@ -1041,20 +1045,18 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
         if (chunk < need) chunk = need;
 
         prof_begin(K_DECODE_PARTIAL, st);
-        hipError_t e = (d == 128 ? v.fn128 : v.fn64)(G, q, kc, vc, pl, max_past_len, ws, nb, n_q, n_kv, S, p.nhc,
-                                                     scale_log2, spm, (int)chunk, window, n_sink, shares, st);
+        hipError_t e = (d == 128 ? v.fn128 : v.fn64)(G, q, kc, vc, pl, max_past_len, ws, dir, recs, nb, n_q, n_kv, S,
+                                                     p.nhc, scale_log2, spm, (int)chunk, window, n_sink, shares, st);
         prof_end(K_DECODE_PARTIAL, st);
         if (e != hipSuccess) return e;
 
         prof_begin(K_DECODE_COMBINE, st);
         if (d == 128)
-            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl,
-                               max_past_len, o, nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk, window, n_sink,
-                               sink_logits, shares);
+            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, dir, recs,
+                               o, n_q, n_kv, p.nhc, p.gc, sink_logits, shares);
         else
-            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, pl,
-                               max_past_len, o, nb, n_q, n_kv, p.nhc, p.gc, G, spm, (int)chunk, window, n_sink,
-                               sink_logits, shares);
+            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, dir, recs,
+                               o, n_q, n_kv, p.nhc, p.gc, sink_logits, shares);
         prof_end(K_DECODE_COMBINE, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
