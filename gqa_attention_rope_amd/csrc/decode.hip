@@ -86,21 +86,22 @@ __device__ __forceinline__ int rows_clamped(const int32_t* past_len, int b, int 
     P = P < 0 ? 0 : (P > pmax ? pmax : P);
     return P + 1;  // rows 0..P
 }
-__device__ __forceinline__ int tiles_of(const int32_t* past_len, int b, int pmax, int window, int n_sink) {
-    return geo_of(rows_clamped(past_len, b, pmax), window, n_sink).nt;
-}
 
-// Exclusive prefix of per-sequence tile counts into s_pre[0..B], 256 sequences
-// per pass with one (clamped, unconditional) load per thread, so every pass
-// costs a single memory round trip.
+// Exclusive prefix of per-sequence tile counts into s_pre[0..B], and each
+// sequence's row count into s_len[0..B-1] (so that no later step reads
+// past_len from memory again), 256 sequences per pass with one (clamped,
+// unconditional) load per thread, so every pass costs a single memory round
+// trip.
 __device__ void tile_prefix(const int32_t* past_len, int B, int pmax, int window, int n_sink, int* s_pre,
-                            int* s_wsum) {
+                            int* s_len, int* s_wsum) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     int carry = 0;
     for (int base = 0; base < B; base += THREADS) {
         const int b = base + tid;
-        const int n = tiles_of(past_len, b < B ? b : B - 1, pmax, window, n_sink);
+        const int L = rows_clamped(past_len, b < B ? b : B - 1, pmax);
+        const int n = geo_of(L, window, n_sink).nt;
+        if (b < B) s_len[b] = L;
         const int mine = b < B ? n : 0;
         int x = mine;
 #pragma unroll
@@ -150,7 +151,8 @@ __device__ __forceinline__ unsigned long long frac_per_wg(const Shares& sh, int 
 // F <= 2^32, so the product fits in 64 bits
 __device__ __forceinline__ long long share_begin(int w, long long Ts, const Shares& sh) {
     if (w >= sh.G) return Ts;
-    int s = w / sh.n_cu;
+    // slot w / n_cu, capped at ns - 1 (compares instead of a division)
+    int s = (w >= sh.n_cu) + (w >= 2 * sh.n_cu) + (w >= 3 * sh.n_cu);
     if (s > sh.ns - 1) s = sh.ns - 1;
     const unsigned long long f = frac_before_slot(sh, s) + (unsigned long long)(w - s * sh.n_cu) * frac_per_wg(sh, s);
     return (long long)(((unsigned long long)Ts * f) >> 32);
@@ -226,7 +228,8 @@ struct Sched {
 __device__ __forceinline__ Sched make_sched(int T_all, int static_pm, int chunk) {
     Sched s;
     s.T_all = T_all;
-    s.Ts = (int)((long long)T_all * static_pm / 1000);
+    // floor(T_all * static_pm / 1000) in 32-bit arithmetic (T_all < 2^31, static_pm <= 1000)
+    s.Ts = (T_all / 1000) * static_pm + (T_all % 1000) * static_pm / 1000;
     s.C = chunk;
     s.n_dyn = (T_all - s.Ts + chunk - 1) / chunk;
     return s;
@@ -262,9 +265,10 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     // state of each wave when a piece ends: o[D], m at D, l at D+1
     __shared__ float s_park[WAVES][HGW][D + 4];
     __shared__ int s_ticket;
-    extern __shared__ int s_pre[];  // B + 1 entries
+    extern __shared__ int s_pre[];  // B + 1 entries, then s_len
+    int* const s_len = s_pre + B + 1;  // B entries
 
-    tile_prefix(past_len, B, pmax, window, n_sink, s_pre, s_wsum);
+    tile_prefix(past_len, B, pmax, window, n_sink, s_pre, s_len, s_wsum);
 
     // values read from LDS are the same in every lane: keep them in scalar registers
     auto uni = [] __attribute__((always_inline)) (int x) { return __builtin_amdgcn_readfirstlane(x); };
@@ -281,20 +285,19 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     const int rbase = rg * C::ROWS_W;
     const int g = n_q / n_kv;
 
-    auto rows_of = [&] __attribute__((always_inline)) (int bb) {
-        int P = past_len[bb];
-        P = P < 0 ? 0 : (P > pmax ? pmax : P);
-        return P + 1;
-    };
-    // cursor of global tile tau: largest b with segs_per_b * s_pre[b] <= tau
+    auto rows_of = [&] __attribute__((always_inline)) (int bb) { return s_len[bb]; };
+    // cursor of global tile tau: the largest b with segs_per_b * s_pre[b] <= tau,
+    // i.e. the number of b in 1 .. B-1 that qualify, counted 64 at a time by
+    // ballot (independent LDS reads instead of a dependent binary search)
     auto cursor_at = [&] __attribute__((always_inline)) (int tau) {
-        int lo = 0, hi = B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (segs_per_b * uni(s_pre[mid]) <= tau) lo = mid; else hi = mid - 1;
+        int cnt = 0;
+        for (int b0 = 1; b0 < B; b0 += 64) {
+            const int bb = b0 + lane;
+            const bool qual = bb < B && segs_per_b * s_pre[bb < B ? bb : 0] <= tau;
+            cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(qual));
         }
         Cursor c;
-        c.b = uni(lo);
+        c.b = uni(cnt);
         c.nt = uni(s_pre[c.b + 1] - s_pre[c.b]);
         const int off = tau - segs_per_b * uni(s_pre[c.b]);
         c.sj = uni(off / c.nt);
@@ -404,7 +407,10 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         }
         const bool tile = ld_left > 0;
         const int rem = tile ? ld_left - 1 : 0;
-        const bool grab = !no_more && !have_next && !pending && rem <= 2;
+        // the next ticket is taken with the range's last tile but one: its value is
+        // read when this stage is consumed two steps later, just in time for the
+        // issue after the range's last tile, and no earlier commitment is made
+        const bool grab = !no_more && !have_next && !pending && rem <= 1;
         const int at = ld.tt < ld.nst ? ld.tt : ld.at0 + (ld.tt - ld.nst);  // absolute tile of this one
         stg.tt = uni(at);
         stg.L = uni(ld.L);
@@ -829,7 +835,7 @@ hipError_t launch_partial_t(int G, const uint16_t* q_rot, const uint16_t* k_cach
                             const int32_t* past_len, int pmax, float* ws, int4* dir, float* recs, int B, int n_q,
                             int n_kv, int S, int nhc, float scale_log2, int static_pm, int chunk, int window,
                             int n_sink, const Shares& shares, hipStream_t st) {
-    const size_t dyn = (size_t)(B + 1) * sizeof(int);
+    const size_t dyn = (size_t)(2 * B + 1) * sizeof(int);
     hipLaunchKernelGGL((decode_partial_kernel<D, HGW, NHG>), dim3(G), dim3(THREADS), dyn, st, q_rot, k_cache,
                        v_cache, past_len, pmax, ws, dir, recs, B, n_q, n_kv, S, nhc, scale_log2, static_pm, chunk,
                        window, n_sink, shares);
@@ -840,7 +846,7 @@ template <int D, int HGW, int NHG>
 int occupancy_t(int B) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_partial_kernel<D, HGW, NHG>, THREADS,
-                                                     (size_t)(B + 1) * sizeof(int)) != hipSuccess)
+                                                     (size_t)(2 * B + 1) * sizeof(int)) != hipSuccess)
         return 1;
     return blocks > 0 ? blocks : 1;
 }
@@ -856,9 +862,10 @@ struct Variant {
     occ_fn occ128, occ64;
 };
 // Default share ratio between dispatch slots, by head groups per workgroup:
-// measured best at 1.5 for one head group (g = 4, 32/8 heads) and 1.2 for two
-// (g = 8, 64/8 heads); the others take 1.2.
-int default_slot_ratio(const Variant& v) { return v.nhg == 1 ? 1500 : 1200; }
+// measured best at 1.4 for one head group (g = 4, 32/8 heads, two workgroups
+// per CU) and 1.2 for two (g = 8, 64/8 heads, three per CU); the others take
+// 1.2.
+int default_slot_ratio(const Variant& v) { return v.nhg == 1 ? 1400 : 1200; }
 
 #define GQA_VARIANT(H, N)                                                                                   \
     Variant {                                                                                               \
@@ -1003,10 +1010,15 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
         if (e != hipSuccess) return e;
     }
     int G = wg_override;
-    // default: as many workgroups as fit on the chip at once (one wave of workgroups)
+    // default: one wave of workgroups, as many as fit on the chip at once, but
+    // at most two per CU for one head group per workgroup (up to 4 heads per
+    // segment): there two already keep HBM busy, and with fewer, longer
+    // workgroups the ones still running at the end finish sooner
     if (G <= 0) {
         const int bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
-        G = cu_count * (d == 128 ? v.occ128(bs) : v.occ64(bs));
+        int per_cu = d == 128 ? v.occ128(bs) : v.occ64(bs);
+        if (v.nhg == 1 && per_cu > 2) per_cu = 2;
+        G = cu_count * per_cu;
     }
     // never more workgroups than tiles: a small problem would otherwise have
     // most workgroups queue on the ticket counter with nothing to do

@@ -40,7 +40,7 @@ hipError_t launch_rope_append(const uint16_t* q, uint16_t* q_rot, const uint16_t
 // ---- decode (split-K partials + combine) ----------------------------------------
 // Largest batch one decode launch handles; larger batches are processed in
 // slices of this many sequences.
-constexpr int DECODE_MAX_B = 2048;
+constexpr int DECODE_MAX_B = 1024;
 // Upper bound on the number of split-K workgroups (sizes the workspace).
 constexpr int DECODE_MAX_WG = 2048;
 // Work schedule of the split-K kernel: this many per-mille of the tiles are

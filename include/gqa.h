@@ -337,7 +337,7 @@ int gqa_set_decode_schedule(int static_permille, int chunk_tiles);
  * ratio_permille / 1000 times that of the next younger slot.  Older residents
  * win instruction issue on a CU and stream faster, so equal shares
  * (ratio_permille = 1000) leave the youngest finishing last.  A value <= 0
- * restores the defaults, which depend on the kernel variant (1500 when a
+ * restores the defaults, which depend on the kernel variant (1400 when a
  * workgroup holds one head group, i.e. up to 4 query heads per segment, and
  * 1200 otherwise); others are
  * clamped to [250, 8000].  Results do not depend on it beyond floating-point
