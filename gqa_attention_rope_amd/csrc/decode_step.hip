@@ -292,11 +292,15 @@ __global__ __launch_bounds__(ST_THREADS) void decode_step_kernel(
     }
 
     // ---- this split's records, then count it on the segment's counter.  The
-    // records are written through to memory (agent-scope relaxed atomic
-    // stores) and each thread waits for its stores to complete before the
-    // workgroup counts itself, so the merging workgroup, which reads them with
-    // agent-scope loads, sees them whichever XCD it runs on.  This avoids a
-    // release fence, which would write back the whole L2 of the XCD.
+    // count is an agent-scope release (thread 0, after the workgroup barrier
+    // that orders every thread's record stores before it), and the workgroup
+    // whose count completes the segment executes an agent-scope acquire fence
+    // before it reads the other splits' records: under the HIP memory model
+    // the records happen-before the merge whichever XCD each split ran on.
+    // The records are agent-scope atomic stores, written through to the
+    // device's point of coherence, so the L2 write-back that the release
+    // performs finds little to write (plain stores measured 2.9 us slower on
+    // one Llama-3.1-8B layer; these 0.9 us slower than relaxed ordering).
     const size_t segi = (size_t)b * n_kv + j;
     float* rec0 = recs + segi * nsplit * g * REC;
 #pragma unroll
@@ -312,12 +316,13 @@ __global__ __launch_bounds__(ST_THREADS) void decode_step_kernel(
         for (int x = 0; x < DPL; ++x)
             __hip_atomic_store(r + 4 + DPL * lane + x, o[k][x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's record stores have completed
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&counters[segi], 1) == nsplit - 1;
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(&counters[segi], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
     __syncthreads();
     if (!s_last) return;
-    auto rd = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    auto rd = [](const float* a) { return *a; };
 
     // ---- last split of the segment: merge in split order.  Lane s holds split
     // s's (m, l); the outputs are read eight splits at a time so the loads

@@ -157,7 +157,7 @@ def test_decode_step_writes_stay_inside_its_buffers(case):
 
 
 def test_sliced_batches_write_inside_their_buffers():
-    """Decode beyond one launch (2048 sequences) and rope_append + prefill beyond the grid limit (65535)."""
+    """Decode beyond one launch (1024 sequences) and rope_append + prefill beyond the grid limit (65535)."""
     B, n_q, n_kv, d, S = 2100, 8, 2, 64, 64
     past = [int(x) for x in np.random.default_rng(15).integers(0, S - 1, size=B)]
     say("guard bands: decode B = 2100")

@@ -807,7 +807,7 @@ def test_decode_step_large_group_both_routes(thr):
 # ---------------------------------------------------------------- launch slicing at the batch limits
 
 def test_decode_batch_beyond_one_launch():
-    """More sequences than one split-K launch takes (2048): the batch runs in slices."""
+    """More sequences than one split-K launch takes (1024): the batch runs in slices."""
     B, n_q, n_kv, d, S = 2100, 8, 2, 64, 64
     past = [int(x) for x in np.random.default_rng(5).integers(0, S - 1, size=B)]
     say("decode B = 2100")
