@@ -3,19 +3,30 @@
 A step is one decode step of a batch of 32 Llama-3.1-8B sequences through 32
 layers: per layer, RoPE + cache append of the new token (gqa_rope_append),
 then split-K decode attention over cache rows 0..past_len[b]
-(gqa_decode_attn).  Contexts are ragged, past_len ~ U[512, 8191] (seeded),
-caches [32, 8, 8192, 128] bf16 per layer, 32 distinct layers (32 GiB).  All
-inputs are resident in HBM before timing starts.
+(gqa_decode_attn: the partials kernel and the combine kernel).  Contexts are
+ragged, past_len ~ U[512, 8191] (seeded), caches [32, 8, 8192, 128] bf16 per
+layer, 32 distinct layers (32 GiB).  All inputs are resident in HBM before
+timing starts.
 
-Printed: one JSON line.  value = KV-read GB/s over the whole step
-(sum over layers and sequences of (past_len+1) * n_kv * d * 2 tensors * 2 B,
-divided by the step time); tokens/s = B / step time.  roofline = the decode
-split-K kernel's algorithmic bytes per launch over its average launch time
-(HIP events on the launch stream), against 8 TB/s; roofline.traffic = HBM bytes
-per launch from the committed rocprofv3 byte-counter summary under profiles/
-(null once the decode kernel sources differ from the ones it was taken on).
-cpu_baseline = the fp64
-oracle on a bounded sample of the same workload, on this host.
+Printed: one JSON line.
+  value = KV-read GB/s over the whole step (sum over layers and sequences of
+    (past_len+1) * n_kv * d * 2 tensors * 2 B, divided by the step time);
+    tokens/s = B / step time.
+  decode_attention = the same KV bytes over the decode attention kernels
+    alone (partials + combine per layer).
+  roofline = decode attention (partials + combine): algorithmic bytes per
+    layer (KV rows + q) over the two kernels' mean launch times, against
+    8 TB/s; roofline.dominant_kernel = the partials kernel alone.  Launch times
+    come from HIP events recorded on the launch stream around every launch
+    (the library's timing hooks); the rocprofv3 kernel trace under profiles/
+    gives the same figures from the profiler.  roofline.traffic = HBM bytes
+    per layer from the committed rocprofv3 byte-counter summary (null once the
+    decode kernel sources differ from the ones it was taken on).
+  stream_read_ceiling = the library's read-only streaming kernel over a
+    buffer of one layer's KV bytes (larger than the 256 MB MALL): the HBM read
+    rate a plain kernel reaches on this machine.
+  cpu_baseline = the fp64 oracle on a bounded sample of the same workload on
+    this host, all cores and one core.
 
 extra (skipped with --no-extra): chunked prefill TFLOP/s (B4, T512 on
 past_len 2048); the 70B-shaped scaled-RoPE decode (B64, 64/8 heads, 80 calls);
@@ -24,6 +35,9 @@ rope_append + decode_attn against the single-launch gqa_decode_step; and
 wide-group decode (B16 64/1 and B32 32/2 heads), the wide kernel against the
 split-K path on the same call.  The small-batch and wide legs time HIP graphs
 of 20 calls replayed back to back, so host launch overhead is excluded.
+"warm" figures replay with the inputs left in the caches by the previous call
+(the small cases fit in the 256 MB MALL); "cold" ones put a 1 GiB write
+between calls inside the graph and subtract a graph of the writes alone.
 """
 
 import argparse
@@ -41,7 +55,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 HEADLINE = "llama8b_b32_decode_32layers"
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "decode_partial_llama8b_b32_decode_32layers_hbm_counters.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_llama8b_b32_decode_32layers_hbm_counters.txt")
 KERNEL_SOURCES = ("gqa_attention_rope_amd/csrc/decode.hip", "gqa_attention_rope_amd/csrc/common.hpp",
                   "gqa_attention_rope_amd/csrc/kernels.hpp", "gqa_attention_rope_amd/build.py")
 
@@ -56,19 +70,24 @@ def kernel_source_hash():
 
 
 def counter_traffic():
-    """HBM bytes per decode split-K launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
-    each counter scaled by its plain-copy calibration factor.  None when the kernel sources have changed
-    since the counters were taken (or the summary is absent)."""
+    """HBM bytes per layer of the decode attention kernels (partials, combine) from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, each counter scaled by its plain-copy calibration factor.  None when the
+    kernel sources have changed since the counters were taken (or the summary is absent)."""
     try:
         with open(COUNTERS) as fh:
-            rec = next(json.loads(l[len("RECORD "):]) for l in fh if l.startswith("RECORD "))
-    except (OSError, StopIteration, ValueError):
+            recs = [json.loads(l[len("RECORD "):]) for l in fh if l.startswith("RECORD ")]
+    except (OSError, ValueError):
+        recs = []
+    if not recs:
         return None, "no counter summary"
-    if rec.get("source_sha256_16") != kernel_source_hash():
+    if any(r.get("source_sha256_16") != kernel_source_hash() for r in recs):
         return None, "decode kernel sources changed since the counters were taken"
-    t = rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]
-    return int(round(t)), "rocprofv3 FETCH_SIZE x%g + WRITE_SIZE x%g (plain-copy calibration), bytes per launch" % (
-        rec["fetch_factor"], rec["write_factor"])
+    out = {}
+    for r in recs:
+        out[r["kernel"]] = int(round(r["fetch_kib"] * 1024 * r["fetch_factor"] + r["write_kib"] * 1024 * r["write_factor"]))
+    f = recs[0]
+    return out, "rocprofv3 FETCH_SIZE x%g + WRITE_SIZE x%g (plain-copy calibration), bytes per launch" % (
+        f["fetch_factor"], f["write_factor"])
 
 
 def parse():
@@ -81,6 +100,7 @@ def parse():
     ap.add_argument("--decode-wg", type=int, default=0, help="override the split-K workgroup count")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="first run one plain device copy of this many GiB (reference for HBM byte counters)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling leg")
     return ap.parse_args()
 
 
@@ -115,11 +135,58 @@ def kernel_avg(gq, fn, steps, kind):
         fn()
     torch.cuda.synchronize()
     gq.gqa_profile_enable(False)
-    out = {k: gq.gqa_profile_read(k) for k in ("rope_append", "decode_partial", "decode_combine", "prefill",
-                                               "decode_step", "decode_wide")}
+    out = {k: gq.gqa_profile_read(k) for k in KINDS}
     gq.gqa_profile_reset()
     ms, n = out[kind]
     return ms / max(n, 1), out
+
+
+KINDS = ("rope_append", "decode_partial", "decode_combine", "prefill", "decode_step", "decode_wide", "stream_read")
+
+
+def call_kernel_us(gq, fn, reps, flush=None):
+    """Per call of fn: the device time of each kernel kind it launches (HIP events around every launch, summed
+    per call, median over reps calls).  With flush, a 1 GiB write runs before each call (not timed), so the
+    call starts with its inputs out of the L2 and the 256 MB MALL ("cold")."""
+    import numpy as np
+    import torch
+    per = {k: [] for k in KINDS}
+    for r in range(reps):
+        if flush is not None:
+            flush.fill_(r & 0xff)
+        torch.cuda.synchronize()
+        gq.gqa_profile_reset()
+        gq.gqa_profile_enable(True)
+        fn()
+        torch.cuda.synchronize()
+        gq.gqa_profile_enable(False)
+        for k in KINDS:
+            ms, n = gq.gqa_profile_read(k)
+            if n:
+                per[k].append(ms * 1e3)
+        gq.gqa_profile_reset()
+    kinds = {k: round(float(np.median(v)), 2) for k, v in per.items() if v}
+    return round(sum(kinds.values()), 2), kinds
+
+
+def stream_ceiling(gq, dev, nbytes):
+    """Best mean launch time of the library's streaming-read kernel over nbytes, across grid sizes."""
+    import torch
+    n = (nbytes + 15) // 16 * 16
+    buf = torch.ones(n, dtype=torch.uint8, device=dev)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    res = {}
+    for wg in (512, 1024, 2048, 4096, 8192):
+        for _ in range(2):
+            gq.gqa_measure_stream_read(buf, sink, wg)
+        ms, _ = kernel_avg(gq, lambda: gq.gqa_measure_stream_read(buf, sink, wg), 20, "stream_read")
+        res[wg] = n / (ms * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    best = max(res, key=res.get)
+    return {"gbs": round(res[best], 1), "pct_hbm_peak": round(100 * res[best] / HBM_PEAK_GBS, 2), "bytes": n,
+            "workgroups": best, "by_workgroups": {str(k): round(v, 1) for k, v in res.items()},
+            "timing": "HIP events around each launch, mean of 20 launches"}
 
 
 def decode_workload(gq, synth, name, dev):
@@ -150,8 +217,14 @@ def decode_workload(gq, synth, name, dev):
                                q_rot=q_rot[l])
             gq.gqa_decode_attn(q_rot[l], kc[c], vc[c], pl, maxp, out=out[l], workspace=ws)
 
+    def attention_only():
+        # the decode attention calls of the step alone, on the q_rot the last step left
+        for l in range(layers):
+            c = l % n_caches
+            gq.gqa_decode_attn(q_rot[l], kc[c], vc[c], pl, maxp, out=out[l], workspace=ws)
+
     info = dict(w=w, B=B, n_q=n_q, n_kv=n_kv, d=d, S=S, layers=layers, past=past,
-                kv_per_layer=kv_bytes(past, n_kv, d), q_bytes=B * n_q * d * 2)
+                kv_per_layer=kv_bytes(past, n_kv, d), q_bytes=B * n_q * d * 2, attention_only=attention_only)
     return step, info, (kc, vc, q, kn, vn)
 
 
@@ -255,35 +328,44 @@ def wide_group_workload(gq, synth, dev, B, n_q, n_kv, seed):
 
 
 def cpu_baseline(info, kc, vc, q, kn, vn):
-    """The fp64 oracle on one layer of the headline step, all 32 sequences."""
+    """The fp64 oracle on one layer of the headline step (all 32 sequences), with every host core this process
+    may use and with one thread."""
     import numpy as np
     from gqa_attention_rope_amd import synth
     from oracle import attend, rope_append
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info, threadpool_limits
+    affinity = len(os.sched_getaffinity(0))
     w = info["w"]
     past = info["past"]
     # host copies of layer 0 (not timed)
     kc0, vc0 = synth.bits(kc[0]), synth.bits(vc[0])
     q0, kn0, vn0 = synth.bits(q[0]), synth.bits(kn[0]), synth.bits(vn[0])
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        qr, kr, vr = rope_append(q0, kn0, vn0, kc0, vc0, past, w["theta"], "interleaved", w["scaling"])
-        attend(qr, kr, vr, past, info["n_kv"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 3:
-            break
-    per_layer = el / reps
-    gbs = info["kv_per_layer"] / per_layer / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one of the 32 layers (all 32 sequences, rope_append + attend in fp64), {reps} rep(s), "
-                      f"{per_layer:.2f} s per layer; tokens/s at that rate over 32 layers: "
-                      f"{info['B'] / (per_layer * info['layers']):.4f}"}
+
+    def run(max_reps, budget_s):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            qr, kr, vr = rope_append(q0, kn0, vn0, kc0, vc0, past, w["theta"], "interleaved", w["scaling"])
+            attend(qr, kr, vr, past, info["n_kv"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > budget_s or reps >= max_reps:
+                return el / reps, reps
+
+    with threadpool_limits(limits=affinity):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        per_all, reps_all = run(3, 10.0)
+    with threadpool_limits(limits=1):
+        per_one, reps_one = run(1, 30.0)
+    kvb = info["kv_per_layer"]
+    tok = lambda per: round(info["B"] / (per * info["layers"]), 4)
+    return {"value": round(kvb / per_all / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one of the 32 layers (all 32 sequences, rope_append + attend in fp64), {reps_all} rep(s), "
+                      f"{per_all:.2f} s per layer with {threads} BLAS threads ({affinity} host CPUs in this "
+                      f"process's affinity); tokens/s at that rate over 32 layers: {tok(per_all)}",
+            "single_thread": {"value": round(kvb / per_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"same layer, {reps_one} rep(s), {per_one:.2f} s per layer; "
+                                        f"tokens/s over 32 layers: {tok(per_one)}"}}
 
 
 def main():
@@ -319,17 +401,37 @@ def main():
     value = kv_step / (ms * 1e-3) / 1e9
     tok_s = info["B"] / (ms * 1e-3)
 
+    # decode attention alone: the 32 layers' gqa_decode_attn calls (partials + combine) back to back
+    attn_layers_ms, _ = timed(info["attention_only"], args.steps, args.warmup, stream)
+    attn_ms = attn_layers_ms / info["layers"]
     avg_ms, per_kind = kernel_avg(gq, step, max(5, args.steps // 5), "decode_partial")
+    comb_ms = per_kind["decode_combine"][0] / max(per_kind["decode_combine"][1], 1)
     alg = info["kv_per_layer"] + info["q_bytes"]
-    achieved = alg / (avg_ms * 1e-3) / 1e9
+    achieved = alg / (attn_ms * 1e-3) / 1e9
+    achieved_p = alg / (avg_ms * 1e-3) / 1e9
     traffic, traffic_note = counter_traffic()
+    t_part = traffic.get("decode_partial_kernel<128,4,1>") if traffic else None
+    t_comb = traffic.get("decode_combine_kernel<128>") if traffic else None
+    t_attn = t_part + t_comb if (t_part is not None and t_comb is not None) else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "traffic_note": traffic_note,
-                "traffic_over_alg": round(traffic / alg, 4) if traffic else None,
-                "kernel": "decode_partial_kernel<128,4,1>", "avg_launch_us": round(avg_ms * 1e3, 2),
-                "alg_bytes_per_launch": alg}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": t_attn, "traffic_note": traffic_note,
+                "traffic_over_alg": round(t_attn / alg, 4) if t_attn else None,
+                "kernel": "decode attention per layer: decode_partial_kernel<128,4,1> + decode_combine_kernel<128>",
+                "avg_launch_us": round(attn_ms * 1e3, 2), "alg_bytes_per_launch": alg,
+                "timing": f"HIP events around {args.steps} x 32 back-to-back gqa_decode_attn calls (two kernels "
+                          f"each), per call",
+                "dominant_kernel": {"kernel": "decode_partial_kernel<128,4,1>", "achieved": round(achieved_p, 1),
+                                    "frac": round(achieved_p / HBM_PEAK_GBS, 4), "avg_launch_us": round(avg_ms * 1e3, 2),
+                                    "traffic": t_part,
+                                    "traffic_over_alg": round(t_part / alg, 4) if t_part else None,
+                                    "timing": "HIP events on the launch stream around each launch, mean over "
+                                              f"{per_kind['decode_partial'][1]} launches (adds the dispatch gap)"}}
     kinds = {k: {"avg_us": round(v[0] / max(v[1], 1) * 1e3, 2), "launches": v[1]} for k, v in per_kind.items() if v[1]}
+    attn_gbs = info["kv_per_layer"] / (attn_ms * 1e-3) / 1e9
+    decode_attention = {"kv_gbs": round(attn_gbs, 1), "pct_hbm_peak": round(100 * attn_gbs / HBM_PEAK_GBS, 2),
+                        "us_per_layer": round(attn_ms * 1e3, 2),
+                        "definition": "KV bytes per layer / time of one gqa_decode_attn call (partials + combine), "
+                                      "from 32-call loops timed with HIP events"}
 
     line = {
         "metric": "decode attn KV-read GB/s (% of HBM peak) + tokens/s, B=32 ragged ctx<=8192",
@@ -351,8 +453,11 @@ def main():
         "tokens_per_s": round(tok_s, 1),
         "wall_s_timed": round(wall, 3),
         "kernels": kinds,
+        "decode_attention": decode_attention,
         "roofline": roofline,
     }
+    if not args.no_ceiling:
+        line["stream_read_ceiling"] = stream_ceiling(gq, dev, info["kv_per_layer"] + info["q_bytes"])
 
     if not args.no_extra:
         extra = {}
@@ -360,11 +465,16 @@ def main():
         pstep, flops = prefill_workload(gq, synth, dev)
         pms, _ = timed(pstep, 20, 3, stream)
         pavg, _ = kernel_avg(gq, pstep, 10, "prefill")
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        p_warm, _ = call_kernel_us(gq, pstep, 20)
+        p_cold, _ = call_kernel_us(gq, pstep, 20, flush)
         extra["chunked_prefill"] = {"workload": "llama8b_chunked_prefill B4 T512 P2048", "ms": round(pms, 4),
                                     "tflops": round(flops / (pms * 1e-3) / 1e12, 1),
                                     "kernel_tflops": round(flops / (pavg * 1e-3) / 1e12, 1),
                                     "frac_mfma_peak": round(flops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                                    "visible_pair_gflop": round(flops / 1e9, 2)}
+                                    "visible_pair_gflop": round(flops / 1e9, 2),
+                                    "kernel_us_warm": p_warm, "kernel_us_cold": p_cold,
+                                    "cold_tflops": round(flops / (p_cold * 1e-6) / 1e12, 1)}
         del pstep
         torch.cuda.empty_cache()
         s5, info5, t5 = decode_workload(gq, synth, "llama70b_shape_decode_scaled", dev)
@@ -381,10 +491,21 @@ def main():
         for name in ("tiny_decode_g3", "llama8b_layer_decode"):
             three, one, kvb, Bs = small_batch_workload(gq, synth, name, dev)
             t3, t1 = graph_us(three), graph_us(one)
+            k3w, _ = call_kernel_us(gq, three, 30)
+            k3c, _ = call_kernel_us(gq, three, 30, flush)
+            k1w, _ = call_kernel_us(gq, one, 30)
+            k1c, _ = call_kernel_us(gq, one, 30, flush)
             small[name] = {"rope_append_plus_decode_us": round(t3, 2), "single_launch_step_us": round(t1, 2),
                            "speedup": round(t3 / t1, 2), "kv_bytes": kvb,
-                           "single_launch_tokens_per_s": round(Bs / (t1 * 1e-6), 1)}
-        extra["small_batch_decode"] = dict(small, timing="HIP graph of 20 steps replayed 20 times, per step")
+                           "single_launch_tokens_per_s": round(Bs / (t1 * 1e-6), 1),
+                           "kernel_us": {"three_call_warm": k3w, "three_call_cold": k3c,
+                                         "single_launch_warm": k1w, "single_launch_cold": k1c}}
+        extra["small_batch_decode"] = dict(
+            small, timing="HIP graph of 20 steps replayed 20 times, per step; kernel_us: sum of the call's kernel "
+                          "times (HIP events around each launch), median of 30 calls, warm = back to back, "
+                          "cold = a 1 GiB write before each call")
+        del flush
+        torch.cuda.empty_cache()
         wide = {}
         for (Bw, nqw, nkvw, seed) in ((16, 64, 1, 1006), (32, 32, 2, 1007)):
             call, kvb = wide_group_workload(gq, synth, dev, Bw, nqw, nkvw, seed)

@@ -40,6 +40,7 @@ EXPORTED = (
     "gqa_decode_step_workspace_bytes",
     "gqa_decode_step",
     "gqa_status_string",
+    "gqa_measure_stream_read",
     "gqa_profile_enable",
     "gqa_profile_read",
     "gqa_profile_reset",
@@ -50,7 +51,7 @@ EXPORTED = (
 )
 
 KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3, "decode_step": 4,
-                "decode_wide": 5}
+                "decode_wide": 5, "stream_read": 6}
 
 
 class GqaAttnOpts(ctypes.Structure):
@@ -113,6 +114,8 @@ def lib():
     L.gqa_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, i32, i32, i32, i32, i32,
                                   ctypes.POINTER(GqaRopeParams), f32, ctypes.POINTER(GqaAttnOpts), vp]
     L.gqa_decode_step.restype = i32
+    L.gqa_measure_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    L.gqa_measure_stream_read.restype = i32
     L.gqa_status_string.argtypes = [i32]
     L.gqa_status_string.restype = ctypes.c_char_p
     L.gqa_profile_enable.argtypes = [i32]
@@ -384,6 +387,13 @@ def gqa_decode_step(q, k_new, v_new, k_cache, v_cache, past_len, max_past_len, t
                                      ctypes.byref(p), float(scale), ctypes.byref(opts) if opts else None,
                                      _stream(stream)))
     return out
+
+
+def gqa_measure_stream_read(buf, sink, workgroups, stream=None):
+    """Read all of ``buf`` (a device tensor, size a multiple of 16 bytes) once with the library's streaming
+    kernel (the HBM read ceiling); ``sink`` is a device int32 tensor of at least ``workgroups`` entries."""
+    _check(lib().gqa_measure_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(workgroups),
+                                         _stream(stream)))
 
 
 def gqa_profile_enable(on=True):

@@ -351,6 +351,17 @@ const char* gqa_status_string(int status) {
     }
 }
 
+int gqa_measure_stream_read(const void* buf, size_t bytes, void* sink, int workgroups, void* stream) {
+    if (!buf || !sink || !aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) || (bytes & 15u) ||
+        workgroups < 1 || workgroups > 65535)
+        return GQA_ERR_INVALID_ARG;
+    int st = ensure_device();
+    if (st != GQA_OK) return st;
+    hipError_t e = gqa::launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink), workgroups,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : hip_status(e);
+}
+
 int gqa_profile_enable(int on) {
     g_prof_on = on != 0;
     return GQA_OK;

@@ -25,7 +25,8 @@ enum KernelKind {
     K_PREFILL = 3,
     K_DECODE_STEP = 4,
     K_DECODE_WIDE = 5,
-    K_KINDS = 6
+    K_STREAM_READ = 6,
+    K_KINDS = 7
 };
 
 // Timing hooks (no-ops unless enabled through gqa_profile_enable).
@@ -111,5 +112,8 @@ hipError_t launch_decode_wide(const uint16_t* q_rot, const uint16_t* k_cache, co
                               const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
                               int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
                               int wg_override, hipStream_t st);
+
+// ---- measurement: a read-only streaming kernel (the HBM read ceiling) ------------
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, hipStream_t st);
 
 }  // namespace gqa

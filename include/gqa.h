@@ -246,8 +246,8 @@ int gqa_prefill_attn_ex(const void* q_rot, const void* k_cache, const void* v_ca
  * Arguments, layouts and ownership as gqa_decode_attn_ex.  Errors:
  * INVALID_ARG, GROUP, HEAD_DIM, RANGE, SCRATCH (the records of the decode
  * path the shape takes need more than GQA_DECODE_NOALLOC_MAX_BYTES: never
- * for sizes where gqa_decode_workspace_bytes() is within it, e.g. B <= 256 at
- * 32/8 heads or B <= 64 at 64/8, d 128; checked on the host, nothing
+ * for sizes where gqa_decode_workspace_bytes() is within it, e.g. any batch at
+ * 32/8 heads or B <= 300 at 64/8, d 128; checked on the host, nothing
  * launched), HIP.
  */
 #define GQA_DECODE_NOALLOC_MAX_BYTES (64u << 20)
@@ -307,12 +307,25 @@ const char* gqa_status_string(int status);
  * the launch stream; gqa_profile_read synchronises those events and returns
  * the summed device time and launch count of one kernel kind.
  *   kind: 0 rope_append, 1 decode split-K partials, 2 decode combine,
- *         3 prefill, 4 single-launch decode step, 5 wide-group decode.
+ *         3 prefill, 4 single-launch decode step, 5 wide-group decode,
+ *         6 the streaming-read measurement kernel.
  * Not thread-safe; for single-threaded benchmark drivers.
  */
 int gqa_profile_enable(int on);
 int gqa_profile_read(int kind, double* total_ms, long long* launches);
 int gqa_profile_reset(void);
+
+/*
+ * Measurement support: the HBM read ceiling that the decode kernels are
+ * compared with.  Reads `bytes` (a multiple of 16) of device memory at `buf`
+ * (16-byte aligned) once, with 16-byte non-temporal loads spread over
+ * `workgroups` workgroups of 256 threads, and writes one 32-bit word per
+ * workgroup to `sink` (device, at least 4 * workgroups bytes) so the loads
+ * are not dropped.  It computes nothing of the attention step.  Errors:
+ * INVALID_ARG (null or misaligned pointer, bytes not a multiple of 16,
+ * workgroups outside 1..65535), HIP.
+ */
+int gqa_measure_stream_read(const void* buf, size_t bytes, void* sink, int workgroups, void* stream);
 
 /*
  * Launch-shape override for tests and tuning: the number of workgroups the

@@ -302,8 +302,8 @@ def decode_noalloc(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), INV), (dict(out=0), INV), (dict(pl=FAKE + 2), INV), (dict(out=FAKE + 8), INV), (dict(B=0), INV),
     (dict(scale=float("nan")), INV), (dict(n_q=6, n_kv=4), GRP), (dict(d=96), HD), (dict(maxp=64), RNG),
-    # 2048 sequences of 32/8 heads: 86.6 MiB of split-K records, beyond the fixed 64 MiB buffer
-    (dict(B=2048, n_q=32, n_kv=8, S=8192, maxp=100), gq.GQA_ERR_SCRATCH),
+    # 1024 sequences of 64/16 heads: 90 MiB of split-K records per launch, beyond the fixed 64 MiB buffer
+    (dict(B=1024, n_q=64, n_kv=16, S=8192, maxp=100), gq.GQA_ERR_SCRATCH),
 ])
 def test_decode_noalloc_rejects_on_host(kw, code):
     assert decode_noalloc(**kw) == code
