@@ -125,6 +125,40 @@ void prof_end(int kind, hipStream_t st) {
 
 }  // namespace gqa
 
+// Pair frequency over the r rotated dims, base^(-2i/r), then the context
+// extension rule ([P7] module L7.4 names PI, NTK, YaRN and Llama-3 scaling;
+// [KV] "Training details that matter" names the Llama-3 fields; the pages give
+// no formulas, so each rule is its published definition):
+//   the wavelength ramp shared by Llama-3 scaling and YaRN: short wavelengths
+//     keep their frequency, long ones are divided by the factor, and the band
+//     between blends the two linearly in original_max_pos / wavelength (the
+//     turns the pair makes over the original context);
+//   position interpolation: every frequency divided by the factor;
+//   NTK-aware scaling only changes the base.
+// Computed in fp64 on the host, once per call: the kernels multiply the
+// position by these values and take sin / cos of the product.
+static double pair_frequency(int i, int r, double base, int sc, const gqa_rope_params* rope) {
+    double f = pow(base, -(2.0 * (double)i) / (double)r);
+    if (sc == GQA_ROPE_SCALING_LLAMA3 || sc == GQA_ROPE_SCALING_YARN) {
+        const double two_pi = 6.283185307179586476925286766559;
+        const double wavelength = two_pi / f;
+        const double long_cut = rope->original_max_pos / rope->low_freq_factor;
+        const double short_cut = rope->original_max_pos / rope->high_freq_factor;
+        if (wavelength < short_cut) {
+            // unchanged
+        } else if (wavelength > long_cut) {
+            f = f / rope->factor;
+        } else {
+            const double s = (rope->original_max_pos / wavelength - rope->low_freq_factor) /
+                             (rope->high_freq_factor - rope->low_freq_factor);
+            f = (1.0 - s) * f / rope->factor + s * f;
+        }
+    } else if (sc == GQA_ROPE_SCALING_LINEAR) {
+        f = f / rope->factor;
+    }
+    return f;
+}
+
 // Validate RoPE parameters for head size d and fill the device-side form.
 static int make_rope(const gqa_rope_params* rope, int d, gqa::RopeDev& rd) {
     if (!(rope->theta > 0.0) || !isfinite(rope->theta)) return GQA_ERR_INVALID_ARG;
@@ -143,37 +177,17 @@ static int make_rope(const gqa_rope_params* rope, int d, gqa::RopeDev& rd) {
     }
     if (!(rope->attn_factor >= 0.0) || !isfinite(rope->attn_factor)) return GQA_ERR_INVALID_ARG;
     const int rdim = rope->rotary_dim == 0 ? d : rope->rotary_dim;
-    if (rdim < 16 || rdim % 16 || rdim > d) return GQA_ERR_INVALID_ARG;
+    if (rdim < 16 || rdim % 16 || rdim > d || rdim / 2 > (int)(sizeof(rd.freq) / sizeof(rd.freq[0])))
+        return GQA_ERR_INVALID_ARG;
     rd.layout = rope->layout;
     rd.rotary_dim = rdim;
-    rd.base = rope->theta;
-    rd.factor = 1.0;
-    rd.low_freq_factor = 1.0;
-    rd.high_freq_factor = 2.0;
-    rd.original_max_pos = 1.0;
-    rd.mode = 0;
     rd.attn = 1.0;
-    switch (sc) {
-        case GQA_ROPE_SCALING_LLAMA3:
-        case GQA_ROPE_SCALING_YARN:
-            rd.mode = 1;
-            rd.factor = rope->factor;
-            rd.low_freq_factor = rope->low_freq_factor;
-            rd.high_freq_factor = rope->high_freq_factor;
-            rd.original_max_pos = rope->original_max_pos;
-            if (sc == GQA_ROPE_SCALING_YARN) rd.attn = 0.1 * log(rope->factor) + 1.0;
-            break;
-        case GQA_ROPE_SCALING_LINEAR:
-            rd.mode = 2;
-            rd.factor = rope->factor;
-            break;
-        case GQA_ROPE_SCALING_NTK:
-            rd.base = rope->theta * pow(rope->factor, (double)rdim / (double)(rdim - 2));
-            break;
-        default:
-            break;
-    }
+    double base = rope->theta;
+    if (sc == GQA_ROPE_SCALING_YARN) rd.attn = 0.1 * log(rope->factor) + 1.0;
+    if (sc == GQA_ROPE_SCALING_NTK) base = rope->theta * pow(rope->factor, (double)rdim / (double)(rdim - 2));
     if (rope->attn_factor > 0.0) rd.attn = rope->attn_factor;
+    for (int i = 0; i < (int)(sizeof(rd.freq) / sizeof(rd.freq[0])); ++i)
+        rd.freq[i] = i < rdim / 2 ? pair_frequency(i, rdim, base, sc, rope) : 0.0;
     return GQA_OK;
 }
 

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(ST_THREADS) void decode_step_kernel(
 
     // ---- angles of position P (fp64), scaled by the attention factor
     for (int i = tid; i < R / 2; i += ST_THREADS) {
-        const double ang = (double)P * pair_frequency(i, R, rp);
+        const double ang = (double)P * rp.freq[i];
         double sn, cs;
         sincos(ang, &sn, &cs);
         s_cos[i] = rp.attn * cs;

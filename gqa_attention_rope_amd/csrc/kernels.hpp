@@ -9,12 +9,13 @@ namespace gqa {
 
 // RoPE parameters as the kernels see them (validated on the host).
 struct RopeDev {
-    double base;  // theta, or the NTK-adjusted base
-    double factor, low_freq_factor, high_freq_factor, original_max_pos;
-    double attn;  // multiplier of the rotated dims
-    int layout;   // 0 interleaved pairs (2i, 2i+1); 1 half pairs (i, i + r/2)
-    int mode;     // 0 plain frequencies; 1 wavelength ramp (Llama-3 / YaRN); 2 divide by factor (PI)
-    int rotary_dim;  // rotated dims r (multiple of 16, <= d)
+    double attn;     // multiplier of the rotated dims
+    int layout;      // 0 interleaved pairs (2i, 2i+1); 1 half pairs (i, i + r/2)
+    int rotary_dim;  // rotated dims r (multiple of 16, <= d <= 128)
+    // angle per position of pair i < r/2 (radians), with the context-extension
+    // rule already applied; position-independent, so the host computes them
+    // once per call and the kernels only multiply by the position
+    double freq[64];
 };
 
 // Kernel kinds for the timing hooks.

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* q, uin
     if (P < 0 || P > max_past_len) return;  // caller error: write nothing for this sequence
     const int pos = P + t;                  // < max_past_len + T <= S (checked on the host)
     for (int i = threadIdx.x; i < R / 2; i += blockDim.x) {
-        double ang = (double)pos * pair_frequency(i, R, rp);
+        double ang = (double)pos * rp.freq[i];
         double sn, cs;
         sincos(ang, &sn, &cs);
         s_cos[i] = rp.attn * cs;  // attention factor (1 unless YaRN or given)

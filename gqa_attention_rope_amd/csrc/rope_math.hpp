@@ -7,38 +7,6 @@
 
 namespace gqa {
 
-// Pair frequency over the r rotated dims, base^(-2i/r), then the context
-// extension rule ([P7] module L7.4 names PI, NTK, YaRN and Llama-3 scaling;
-// [KV] "Training details that matter" names the Llama-3 fields; the pages give
-// no formulas, so each rule is its published definition):
-//   mode 1, the wavelength ramp shared by Llama-3 scaling and YaRN: short
-//     wavelengths keep their frequency, long ones are divided by the factor,
-//     and the band between blends the two linearly in original_max_pos /
-//     wavelength (the turns the pair makes over the original context);
-//   mode 2, position interpolation: every frequency divided by the factor;
-//   NTK-aware scaling only changes the base, which the host has already done.
-__device__ inline double pair_frequency(int i, int r, const RopeDev& rp) {
-    double f = pow(rp.base, -(2.0 * (double)i) / (double)r);
-    if (rp.mode == 1) {
-        const double two_pi = 6.283185307179586476925286766559;
-        double wavelength = two_pi / f;
-        double long_cut = rp.original_max_pos / rp.low_freq_factor;
-        double short_cut = rp.original_max_pos / rp.high_freq_factor;
-        if (wavelength < short_cut) {
-            // unchanged
-        } else if (wavelength > long_cut) {
-            f = f / rp.factor;
-        } else {
-            double s = (rp.original_max_pos / wavelength - rp.low_freq_factor) /
-                       (rp.high_freq_factor - rp.low_freq_factor);
-            f = (1.0 - s) * f / rp.factor + s * f;
-        }
-    } else if (rp.mode == 2) {
-        f = f / rp.factor;
-    }
-    return f;
-}
-
 // (a, b) -> (a cos - b sin, a sin + b cos), fp64, each output rounded once to bf16.
 __device__ __forceinline__ void turn(float a, float b, double c, double s, uint32_t& ra, uint32_t& rb) {
     double da = (double)a, db = (double)b;
