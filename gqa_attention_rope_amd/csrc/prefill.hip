@@ -19,11 +19,14 @@
 //                  part and a bf16 remainder so that the weights enter the
 //                  product with ~16 significant bits)
 // K and V tiles go from HBM straight into LDS (range-checked buffer loads with
-// the LDS destination, no register staging), double-buffered: the next
-// tile's loads are in flight while the current one is computed, and one
-// workgroup barrier per tile both publishes the new tile and frees the old
-// buffer.  Tiles entirely above every row's causal bound are never loaded;
-// tiles that straddle a bound are masked element-wise.
+// the LDS destination, no register staging), each in its own double buffer
+// with V one tile behind K, and one workgroup barrier per tile both publishes
+// the new tiles and frees the old buffers.  The loop is software-pipelined:
+// the score MFMAs of tile j+1 run while the weights of tile j are formed, and
+// the second half of those weights while the first half goes through P V, so
+// that exponentials and conversions overlap matrix work.  Tiles entirely
+// above every row's causal bound are never loaded; tiles that straddle a
+// bound are masked element-wise.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "lds_direct.hpp"
@@ -49,6 +52,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ out, int n_q, int n_kv, int T,
                                                           int S, int hpw, int tq, int n_tq, float scale_log2,
                                                           int window, int n_sink, const float* sink_logits) {
+    static_assert(D == 64 || D == 128, "head sizes 64 and 128");
     constexpr int PPR = D / 8;                 // 16-byte pieces per key row
     constexpr int KS = D / 32;                 // MFMA k-steps over d
     constexpr int DB = D / 16;                 // 16-dim blocks of the output
@@ -157,15 +161,6 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
         dma_off[x] = r * ROW_B + c * 16;
     }
     const uint32_t lds_base = lds_addr(smem);
-    auto load = [&](int tile, int buf) {
-        const int soff = tile * TILE_B;
-#pragma unroll
-        for (int x = 0; x < DMA_N; ++x) {
-            const uint32_t dst = lds_base + (uint32_t)((x * NTHR + wave * 64) * 16);
-            load_lds16(rk, dst + (uint32_t)(buf * TILE_B), dma_off[x], soff);
-            load_lds16(rv, dst + (uint32_t)((2 + buf) * TILE_B), dma_off[x], soff);
-        }
-    };
     // S operand: lane reads key row 16 mb + l16, piece 4 ks + lq.
     int k_rd[KS];
 #pragma unroll
@@ -190,16 +185,124 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
     auto tile_of = [&](int it) { return it < nst ? it : wt0 + (it - nst); };
-    load(tile_of(0), 0);
-    for (int it = 0; it < n_iter; ++it) {
-        const int tile = tile_of(it);
-        const int buf = it & 1;
-        // this wave's loads of the tile are done; after the barrier every
-        // wave's are, and every wave has finished the previous tile, whose
-        // buffers the next loads overwrite
+    auto load_k = [&](int tile, int buf) {
+        const int soff = tile * TILE_B;
+#pragma unroll
+        for (int x = 0; x < DMA_N; ++x)
+            load_lds16(rk, lds_base + (uint32_t)((x * NTHR + wave * 64) * 16 + buf * TILE_B), dma_off[x], soff);
+    };
+    auto load_v = [&](int tile, int buf) {
+        const int soff = tile * TILE_B;
+#pragma unroll
+        for (int x = 0; x < DMA_N; ++x)
+            load_lds16(rv, lds_base + (uint32_t)((x * NTHR + wave * 64) * 16 + (2 + buf) * TILE_B), dma_off[x],
+                       soff);
+    };
+
+    // S^T = K Q^T for 64 keys x 32 query rows, in one block (used where nothing
+    // runs beside it)
+    auto qk = [&](const unsigned char* ktile, f32x4_t (&s)[4][2]) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktile + k_rd[ks] + 16 * mb * ROW_B);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[nb][ks], s[mb][nb], 0, 0, 0);
+            }
+        }
+    };
+    // hide the keys of a tile that cross a row's causal bound (or left its window)
+    auto mask = [&](int tile, f32x4_t (&s)[4][2]) {
+        const int key0 = tile * KT;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int lim = P + row_t[nb];                   // last visible key of this row
+            const int wlo = window > 0 ? lim - window : -1;  // keys at or below it left the window
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = key0 + 16 * mb + 4 * lq + i;
+                    // bitwise, not short-circuit: a select per score instead of a branch
+                    const bool hide = (key > lim) | ((key <= wlo) & (key >= n_sink));
+                    s[mb][nb][i] = hide ? -INFINITY : s[mb][nb][i];
+                }
+        }
+    };
+    // raw score maximum of row block nb: v_maximum3 needs no canonicalising of its
+    // inputs (fmaxf does); lanes l, l ^ 16, l ^ 32 and l ^ 48 hold the same query
+    // row, so two in-register lane swaps finish it
+    auto rowmax_part = [&](const f32x4_t (&s)[4][2], int nb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+            mx = __builtin_elementwise_maximum(
+                mx, __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[mb][nb][0], s[mb][nb][1]),
+                                                  __builtin_elementwise_maximum(s[mb][nb][2], s[mb][nb][3])));
+        return mx;
+    };
+    auto rowmax_finish = [&](float mx) {
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = __builtin_elementwise_maximum(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        return __builtin_elementwise_maximum(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    };
+    // [hi/lo][kb][nb]: the weights as PV B operands, split p = hi + lo with both parts
+    // in bf16 so the product with V keeps ~16 significant bits of p
+    u32x4_t pk[2][2][2];
+    // weights of scores 2 ip, 2 ip + 1 of block (mb, nb) against the exponent
+    // reference mref; their sum goes to ps
+    auto wpair = [&](const f32x4_t (&s)[4][2], int mb, int nb, int ip, const float (&mref)[2], float (&ps)[2]) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[mb][nb][2 * ip], scale_log2, -mref[nb]));
+        const float p1 = fast_exp2(__builtin_fmaf(s[mb][nb][2 * ip + 1], scale_log2, -mref[nb]));
+        ps[nb] += p0 + p1;
+        const uint32_t h = cvt_pk_bf16(p0, p1);
+        const uint32_t l = cvt_pk_bf16(p0 - bf_lo(h), p1 - bf_hi(h));
+        pk[0][mb >> 1][nb][(mb & 1) * 2 + ip] = h;
+        pk[1][mb >> 1][nb][(mb & 1) * 2 + ip] = l;
+    };
+    // the 8 score pairs of keys 32 kb .. 32 kb + 31, in the order they are formed
+    auto wpair_k = [&](const f32x4_t (&s)[4][2], int kb, int c, const float (&mref)[2], float (&ps)[2]) {
+        wpair(s, 2 * kb + (c >> 2), (c >> 1) & 1, c & 1, mref, ps);
+    };
+    // V^T operand of keys 32 kb .. 32 kb + 31 and dims 16 db .. 16 db + 15
+    auto vread = [&](const unsigned char* vtile, int kb, int db) {
+        const i16x4_t u0 = read_tr16(vtile + v_rd[db] + 32 * kb * ROW_B);
+        const i16x4_t u1 = read_tr16(vtile + v_rd[db] + (32 * kb + 16) * ROW_B);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto pv_mfma = [&](const bf16x8_t& a, int kb, int db, int hl) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+            oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8_t, pk[hl][kb][nb]), oacc[db][nb], 0, 0, 0);
+    };
+    // The order below is fixed by hand (sched_barrier): left to itself the
+    // compiler issues all MFMAs of a phase back to back and the exponentials
+    // after them, so the matrix pipe and the VALU take turns instead of
+    // working together.  The LDS operands of each MFMA are read one slot
+    // ahead.
+#define PF_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+    // K and V tiles sit in separate double buffers with V one tile behind K.
+    // Iteration it holds the scores of tile it in registers.  Phase A runs the
+    // score MFMAs of tile it+1 with the weights of keys 0..31 of tile it formed
+    // between them; phase B runs P V over keys 0..31 with the weights of keys
+    // 32..63 formed between, then P V over keys 32..63 with the row maxima of
+    // tile it+1 (its raw scores; a tile that needs a mask recomputes them).
+    float mx_cur[2];
+    auto iter = [&](int it, f32x4_t (&cur)[4][2], f32x4_t (&nxt)[4][2]) {
+        // this wave's loads are done; after the barrier every wave's are (V(it),
+        // K(it+1)), and every wave has finished iteration it-1, so the buffers of
+        // K(it) and V(it-1) are free for the next loads
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (it + 1 < n_iter) load(tile_of(it + 1), buf ^ 1);
+        if (it + 2 < n_iter) load_k(tile_of(it + 2), it & 1);
+        if (it + 1 < n_iter) load_v(tile_of(it + 1), (it + 1) & 1);
         // Issue priority grows with the tiles left: of two workgroups sharing
         // a CU the one with more work left is served first, so both tend to
         // finish together instead of the second running alone (one wave per
@@ -211,116 +314,110 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_kernel(const uint16_t* __rest
             else if (rem > 4) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
         }
-        const unsigned char* ktile = smem + buf * TILE_B;
-        const unsigned char* vtile = smem + (2 + buf) * TILE_B;
-
-        // ---- S^T = K Q^T for 64 keys x 32 query rows
-        f32x4_t sacc[4][2];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) sacc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktile + k_rd[ks] + 16 * mb * ROW_B);
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    sacc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[nb][ks], sacc[mb][nb], 0, 0, 0);
-            }
-        }
-
-        // ---- mask (only tiles that cross a row's causal bound), online softmax per query row
-        const int key0 = tile * KT;
+        const int tile = tile_of(it);
         if (tile >= first_masked_tile || window > 0) {
+            mask(tile, cur);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int lim = P + row_t[nb];  // last visible key of this row
-                const int wlo = window > 0 ? lim - window : -1;  // keys at or below it left the window
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = key0 + 16 * mb + 4 * lq + i;
-                        // bitwise, not short-circuit: a select per score instead of a branch
-                        const bool hide = (key > lim) | ((key <= wlo) & (key >= n_sink));
-                        sacc[mb][nb][i] = hide ? -INFINITY : sacc[mb][nb][i];
-                    }
-            }
+            for (int nb = 0; nb < 2; ++nb) mx_cur[nb] = rowmax_finish(rowmax_part(cur, nb));
         }
-        // [hi/lo][kb][nb]: the weights as PV B operands, split p = hi + lo with both parts
-        // in bf16 so the product with V keeps ~16 significant bits of p
-        u32x4_t pk[2][2][2];
+        // The exponent reference m_ref (scaled, base 2) only moves when the row
+        // maximum exceeds it by more than 8: weights then stay below 2^8, and
+        // the accumulators are rescaled rarely instead of on every tile.
+        float mref[2], alpha[2], ps[2] = {0.f, 0.f};
+        bool move[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            float mx = -INFINITY;
-#pragma unroll
-            // v_maximum3 needs no canonicalising of its inputs (fmaxf does)
-            for (int mb = 0; mb < 4; ++mb)
-                mx = __builtin_elementwise_maximum(
-                    mx, __builtin_elementwise_maximum(
-                            __builtin_elementwise_maximum(sacc[mb][nb][0], sacc[mb][nb][1]),
-                            __builtin_elementwise_maximum(sacc[mb][nb][2], sacc[mb][nb][3])));
-            // lanes l, l ^ 16, l ^ 32 and l ^ 48 hold the same query row: two
-            // in-register lane swaps instead of LDS permutes
-            const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = __builtin_elementwise_maximum(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
-            const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = __builtin_elementwise_maximum(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
-            // The exponent reference m_ref (scaled, base 2) only moves when the row
-            // maximum exceeds it by more than 8: weights then stay below 2^8, and
-            // the accumulators are rescaled rarely instead of on every tile.
-            const float mxs = mx * scale_log2;
-            const bool move = mxs > m_run[nb] + 8.f;
-            const float mn = move ? mxs : m_run[nb];
-            const float alpha = move ? fast_exp2(m_run[nb] - mn) : 1.f;
+            const float mxs = mx_cur[nb] * scale_log2;
+            move[nb] = mxs > m_run[nb] + 8.f;
+            const float mn = move[nb] ? mxs : m_run[nb];
+            alpha[nb] = move[nb] ? fast_exp2(m_run[nb] - mn) : 1.f;
             m_run[nb] = mn;
             // a row that has seen no key yet (possible under a window) keeps weight 0
-            const float mref = mn == -INFINITY ? 0.f : mn;
-            float ps = 0.f;
+            mref[nb] = mn == -INFINITY ? 0.f : mn;
+        }
+        if (__builtin_amdgcn_ballot_w64(move[0] | move[1]) != 0) {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                float p[4];
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(__builtin_fmaf(sacc[mb][nb][i], scale_log2, -mref));
-                    ps += p[i];
-                }
-                const uint32_t h01 = cvt_pk_bf16(p[0], p[1]), h23 = cvt_pk_bf16(p[2], p[3]);
-                const uint32_t l01 = cvt_pk_bf16(p[0] - bf_lo(h01), p[1] - bf_hi(h01));
-                const uint32_t l23 = cvt_pk_bf16(p[2] - bf_lo(h23), p[3] - bf_hi(h23));
-                const int w0 = (mb & 1) * 2;
-                pk[0][mb >> 1][nb][w0] = h01;
-                pk[0][mb >> 1][nb][w0 + 1] = h23;
-                pk[1][mb >> 1][nb][w0] = l01;
-                pk[1][mb >> 1][nb][w0 + 1] = l23;
-            }
-            l_run[nb] = l_run[nb] * alpha + ps;
-            if (__builtin_amdgcn_ballot_w64(move) != 0) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db][nb] *= alpha;
-            }
+                for (int nb = 0; nb < 2; ++nb) oacc[db][nb] *= alpha[nb];
         }
 
-        // ---- O^T += V^T P^T
+        // ---- phase A: 4 KS slots (k-step ks, key block mb), two MFMAs each,
+        // with the 8 weight pairs of keys 0..31 spread over them
+        {
+            const unsigned char* ktile = smem + ((it + 1) & 1) * TILE_B;
+            bf16x8_t ka[2];
+            auto kread = [&](int slot) {
+                return *reinterpret_cast<const bf16x8_t*>(ktile + k_rd[slot >> 2] + 16 * (slot & 3) * ROW_B);
+            };
+            ka[0] = kread(0);
+            PF_FENCE();
+            constexpr int NSLOT = 4 * KS;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            bf16x8_t bop[2][2];
+            for (int slot = 0; slot < NSLOT; ++slot) {
+                if (slot + 1 < NSLOT) ka[(slot + 1) & 1] = kread(slot + 1);
+                const int ks = slot >> 2, mb = slot & 3;
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl)
+                for (int nb = 0; nb < 2; ++nb)
+                    nxt[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ka[slot & 1], qop[nb][ks], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : nxt[mb][nb], 0, 0, 0);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) bop[hl][nb] = __builtin_bit_cast(bf16x8_t, pk[hl][kb][nb]);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const i16x4_t u0 = read_tr16(vtile + v_rd[db] + 32 * kb * ROW_B);
-                const i16x4_t u1 = read_tr16(vtile + v_rd[db] + (32 * kb + 16) * ROW_B);
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[0][nb], oacc[db][nb], 0, 0, 0);
-                    oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[1][nb], oacc[db][nb], 0, 0, 0);
-                }
+                for (int c = slot * 8 / NSLOT; c < (slot + 1) * 8 / NSLOT; ++c) wpair_k(cur, 0, c, mref, ps);
+                PF_FENCE();
             }
         }
+        // ---- phase B: P V over keys 0..31 (a weight pair of keys 32..63 per
+        // 16-dim block), then over keys 32..63 (the row maxima of tile it+1)
+        const unsigned char* vtile = smem + (2 + (it & 1)) * TILE_B;
+        {
+            bf16x8_t va[2];
+            va[0] = vread(vtile, 0, 0);
+            PF_FENCE();
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                if (db + 1 < DB) va[(db + 1) & 1] = vread(vtile, 0, db + 1);
+                pv_mfma(va[db & 1], 0, db, 0);
+                pv_mfma(va[db & 1], 0, db, 1);
+#pragma unroll
+                for (int c = db * 8 / DB; c < (db + 1) * 8 / DB; ++c) wpair_k(cur, 1, c, mref, ps);
+                PF_FENCE();
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) l_run[nb] = l_run[nb] * alpha[nb] + ps[nb];
+        {
+            bf16x8_t va[2];
+            float mxp[2];
+            va[0] = vread(vtile, 1, 0);
+            PF_FENCE();
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                if (db + 1 < DB) va[(db + 1) & 1] = vread(vtile, 1, db + 1);
+                pv_mfma(va[db & 1], 1, db, 0);
+                pv_mfma(va[db & 1], 1, db, 1);
+                constexpr int Q4 = DB / 4;  // the four steps of the row maxima, one per quarter
+                if (db == Q4 - 1) mxp[0] = rowmax_part(nxt, 0);
+                if (db == 2 * Q4 - 1) mxp[1] = rowmax_part(nxt, 1);
+                if (db == 3 * Q4 - 1) mx_cur[0] = rowmax_finish(mxp[0]);
+                if (db == 4 * Q4 - 1) mx_cur[1] = rowmax_finish(mxp[1]);
+                PF_FENCE();
+            }
+        }
+    };
+#undef PF_FENCE
+
+    f32x4_t sA[4][2], sB[4][2];
+    load_k(tile_of(0), 0);
+    load_v(tile_of(0), 0);
+    if (n_iter > 1) load_k(tile_of(1), 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(smem, sA);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) mx_cur[nb] = rowmax_finish(rowmax_part(sA, nb));
+    for (int it = 0; it < n_iter; it += 2) {
+        iter(it, sA, sB);
+        if (it + 1 < n_iter) iter(it + 1, sB, sA);
     }
 
     // ---- normalise and store: lane holds dims 16db + 4*lq + 0..3 of its row
