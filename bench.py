@@ -101,6 +101,8 @@ def parse():
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="first run one plain device copy of this many GiB (reference for HBM byte counters)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling leg")
+    ap.add_argument("--legs", default="prefill,long,small,wide",
+                    help="extra legs to run (comma list of prefill, long, small, wide)")
     return ap.parse_args()
 
 
@@ -459,13 +461,15 @@ def main():
     if not args.no_ceiling:
         line["stream_read_ceiling"] = stream_ceiling(gq, dev, info["kv_per_layer"] + info["q_bytes"])
 
+    legs = set(x.strip() for x in args.legs.split(",") if x.strip())
     if not args.no_extra:
         extra = {}
         torch.cuda.synchronize()
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    if not args.no_extra and "prefill" in legs:
         pstep, flops = prefill_workload(gq, synth, dev)
         pms, _ = timed(pstep, 20, 3, stream)
         pavg, _ = kernel_avg(gq, pstep, 10, "prefill")
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         p_warm, _ = call_kernel_us(gq, pstep, 20)
         p_cold, _ = call_kernel_us(gq, pstep, 20, flush)
         extra["chunked_prefill"] = {"workload": "llama8b_chunked_prefill B4 T512 P2048", "ms": round(pms, 4),
@@ -477,6 +481,7 @@ def main():
                                     "cold_tflops": round(flops / (p_cold * 1e-6) / 1e12, 1)}
         del pstep
         torch.cuda.empty_cache()
+    if not args.no_extra and "long" in legs:
         s5, info5, t5 = decode_workload(gq, synth, "llama70b_shape_decode_scaled", dev)
         ms5, _ = timed(s5, 5, 1, stream)
         kv5 = info5["kv_per_layer"] * info5["layers"]
@@ -487,6 +492,7 @@ def main():
             "tokens_per_s": round(info5["B"] / (ms5 * 1e-3), 1)}
         del s5, t5
         torch.cuda.empty_cache()
+    if not args.no_extra and "small" in legs:
         small = {}
         for name in ("tiny_decode_g3", "llama8b_layer_decode"):
             three, one, kvb, Bs = small_batch_workload(gq, synth, name, dev)
@@ -504,8 +510,7 @@ def main():
             small, timing="HIP graph of 20 steps replayed 20 times, per step; kernel_us: sum of the call's kernel "
                           "times (HIP events around each launch), median of 30 calls, warm = back to back, "
                           "cold = a 1 GiB write before each call")
-        del flush
-        torch.cuda.empty_cache()
+    if not args.no_extra and "wide" in legs:
         wide = {}
         for (Bw, nqw, nkvw, seed) in ((16, 64, 1, 1006), (32, 32, 2, 1007)):
             call, kvb = wide_group_workload(gq, synth, dev, Bw, nqw, nkvw, seed)
@@ -520,6 +525,9 @@ def main():
             torch.cuda.empty_cache()
         extra["wide_group_decode"] = dict(wide, context="past_len U[2048,8191] seeded, d 128, S 8192",
                                           timing="HIP graph of 20 calls replayed 20 times, per call")
+    if not args.no_extra:
+        del flush
+        torch.cuda.empty_cache()
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(info, *tensors)
