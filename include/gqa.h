@@ -211,6 +211,12 @@ int gqa_prefill_attn(const void* q_rot, const void* k_cache, const void* v_cache
  * With the _ex entry points the decode kernel visits only the tiles holding
  * visible rows, so a window makes the KV read O(window); the prefill kernel
  * skips tiles that lie wholly between the sinks and the earliest window.
+ * Rows are read in 64-row tiles.  A row of a read tile that a query does not
+ * see enters that query's sums with weight zero, and zero times Inf or NaN
+ * is NaN, so every row of a read tile must be finite.  Under a window, the
+ * tiles that hold no row visible to any query of the call (those wholly
+ * between the sink tiles and the window of the query at past_len) are never
+ * read and may hold anything.
  */
 typedef struct gqa_attn_opts {
     int window;

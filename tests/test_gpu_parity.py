@@ -80,6 +80,24 @@ def make_inputs(B, n_q, n_kv, T, d, S, past, seed):
     return q, kn, vn, kc, vc
 
 
+def poison_unread_tiles(caches, past, W, NS):
+    """Under a window of W rows with NS sinks, fill with bf16 NaN the 64-row tiles that hold no row visible to
+    any query of the call: those wholly between the sink tiles and the window of the earliest query (position
+    past_len, which sees rows past_len - W + 1 .. past_len).  The kernels must not read them.  Returns the
+    number of rows filled per cache."""
+    n = 0
+    for b, P in enumerate(past):
+        w0 = P - W + 1
+        if W <= 0 or w0 <= NS:
+            continue
+        lo, hi = -(-NS // 64) * 64, (w0 // 64) * 64
+        if hi > lo:
+            for c in caches:
+                c[b, :, lo:hi] = synth.NAN_BF16
+            n += hi - lo
+    return n
+
+
 # ---------------------------------------------------------------- rope_append
 
 APPEND_CASES = [
@@ -549,6 +567,7 @@ def test_decode_window_and_sinks(case):
         vc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 1300 + b))
     sinks = np.random.default_rng(W + NS).standard_normal(n_q).astype(np.float32) if learned else None
     ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    say(f"  {poison_unread_tiles((kc, vc), past, W, NS)} unread rows NaN-filled")
     sk = torch.from_numpy(sinks).to(DEV) if learned else None
     for sched in ((-1, 0), (0, 1), (1000, 2)):
         gq.gqa_set_decode_schedule(*sched)
@@ -578,6 +597,7 @@ def test_prefill_window_and_sinks(case):
     q, _, _, kc, vc = make_inputs(B, n_q, n_kv, T, d, S, past, seed=1400 + W)
     sinks = np.random.default_rng(3 * W + NS).standard_normal(n_q).astype(np.float32) if learned else None
     ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    say(f"  {poison_unread_tiles((kc, vc), past, W, NS)} unread rows NaN-filled")
     sk = torch.from_numpy(sinks).to(DEV) if learned else None
     out = gq.gqa_prefill_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), window=W, n_sink=NS,
                               sink_logits=sk)
@@ -612,6 +632,8 @@ def run_step(case, seed, ws=None):
     sinks = np.random.default_rng(seed).standard_normal(n_q).astype(np.float32) if learned else None
     q_ref, kc_ref, vc_ref = rope_append(q, kn, vn, kc, vc, past, theta, layout, scaling, rotary_dim=rdim)
     ref = attend(q_ref, kc_ref, vc_ref, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    if poison_unread_tiles((kc, vc, kc_ref, vc_ref), past, W, NS):
+        say("  unread window tiles NaN-filled")
     kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
     q_rot = torch.empty(B, n_q, 1, d, dtype=torch.bfloat16, device=DEV)
     out = gq.gqa_decode_step(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling, rdim,
@@ -743,8 +765,9 @@ def test_wide_group_decode_window_sinks_and_paths():
         vc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 1620 + b))
     sinks = np.random.default_rng(3).standard_normal(n_q).astype(np.float32)
     sk = torch.from_numpy(sinks).to(DEV)
-    qd, kd, vd, pl = dev(q), dev(kc), dev(vc), past_dev(past)
     ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    assert poison_unread_tiles((kc, vc), past, W, NS) > 0
+    qd, kd, vd, pl = dev(q), dev(kc), dev(vc), past_dev(past)
     ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
     o1 = gq.gqa_decode_attn(qd, kd, vd, pl, max(past), workspace=ws, window=W, n_sink=NS, sink_logits=sk)
     o2 = gq.gqa_decode_attn(qd, kd, vd, pl, max(past), workspace=ws, window=W, n_sink=NS, sink_logits=sk)
@@ -865,6 +888,7 @@ def test_wide_group_decode_d64_window():
     q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=2201)
     sinks = np.random.default_rng(7).standard_normal(n_q).astype(np.float32)
     ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    assert poison_unread_tiles((kc, vc), past, W, NS) > 0
     out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), window=W, n_sink=NS,
                              sink_logits=torch.from_numpy(sinks).to(DEV))
     torch.cuda.synchronize()
