@@ -308,25 +308,43 @@ def graph_us(fn, per_graph=20, replays=20):
     return a.elapsed_time(b) * 1e3 / (replays * per_graph)
 
 
-def wide_group_workload(gq, synth, dev, B, n_q, n_kv, seed):
-    """Decode attention for a wide query group (g = n_q / n_kv >= 16), ragged contexts U[2048, 8191]."""
+def wide_group_workload(gq, synth, dev, B, n_q, n_kv, seed, cold_bytes=6.4e8):
+    """Decode attention for a wide query group (g = n_q / n_kv >= 16), ragged contexts U[2048, 8191].
+
+    Returns (warm, cold, kv bytes per call, layers): warm repeats the call on one cache pair, whose rows
+    then partly stay in the 256 MB MALL; cold moves to the next of `layers` cache pairs on every call (as
+    the layers of a decode step do), with enough layers that about cold_bytes of K/V lie between two reads
+    of the same rows."""
+    import math
     import torch
     d, S = 128, 8192
     past = synth.past_lengths(B, ("uniform", 2048, 8191), seed)
-    kc = torch.empty((B, n_kv, S, d), dtype=torch.bfloat16, device=dev)
-    vc = torch.empty_like(kc)
-    synth.fill_normal_bf16_(kc, seed * 1000)
-    synth.fill_normal_bf16_(vc, seed * 1000 + 1)
+    kvb = kv_bytes(past, n_kv, d)
+    layers = max(2, math.ceil(cold_bytes / kvb))
+    kcs, vcs = [], []
+    for l in range(layers):
+        kc = torch.empty((B, n_kv, S, d), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        synth.fill_normal_bf16_(kc, seed * 1000 + 2 * l)
+        synth.fill_normal_bf16_(vc, seed * 1000 + 2 * l + 1)
+        kcs.append(kc)
+        vcs.append(vc)
     q = synth.normal_bf16((B, n_q, 1, d), seed + 11, dev)
     pl = torch.as_tensor(past, device=dev)
     maxp = int(past.max())
     out = torch.empty_like(q)
     ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=dev)
+    nxt = [0]
 
-    def call():
-        gq.gqa_decode_attn(q, kc, vc, pl, maxp, out=out, workspace=ws)
+    def warm():
+        gq.gqa_decode_attn(q, kcs[0], vcs[0], pl, maxp, out=out, workspace=ws)
 
-    return call, kv_bytes(past, n_kv, d)
+    def cold():
+        l = nxt[0] % layers
+        nxt[0] += 1
+        gq.gqa_decode_attn(q, kcs[l], vcs[l], pl, maxp, out=out, workspace=ws)
+
+    return warm, cold, kvb, layers
 
 
 def cpu_baseline(info, kc, vc, q, kn, vn):
@@ -513,18 +531,25 @@ def main():
     if not args.no_extra and "wide" in legs:
         wide = {}
         for (Bw, nqw, nkvw, seed) in ((16, 64, 1, 1006), (32, 32, 2, 1007)):
-            call, kvb = wide_group_workload(gq, synth, dev, Bw, nqw, nkvw, seed)
-            t_wide = graph_us(call)
-            gq.gqa_set_decode_wide_min_group(65)  # the split-K path on the same call
-            t_split = graph_us(call)
+            warm, cold, kvb, layers = wide_group_workload(gq, synth, dev, Bw, nqw, nkvw, seed)
+            t_cold = graph_us(cold)
+            t_warm = graph_us(warm)
+            gq.gqa_set_decode_wide_min_group(65)  # the split-K path on the same calls
+            t_split = graph_us(cold)
             gq.gqa_set_decode_wide_min_group(0)
             wide[f"B{Bw}_{nqw}q_{nkvw}kv_g{nqw // nkvw}"] = {
-                "wide_kernel_us": round(t_wide, 2), "kv_gbs": round(kvb / (t_wide * 1e-6) / 1e9, 1),
-                "split_k_us": round(t_split, 2), "speedup": round(t_split / t_wide, 2), "kv_bytes": kvb}
-            del call
+                "wide_kernel_us": round(t_cold, 2), "kv_gbs": round(kvb / (t_cold * 1e-6) / 1e9, 1),
+                "frac_hbm_peak": round(kvb / (t_cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "warm_us": round(t_warm, 2), "warm_kv_gbs": round(kvb / (t_warm * 1e-6) / 1e9, 1),
+                "split_k_us": round(t_split, 2), "speedup": round(t_split / t_cold, 2), "kv_bytes": kvb,
+                "cache_layers": layers}
+            del warm, cold
             torch.cuda.empty_cache()
-        extra["wide_group_decode"] = dict(wide, context="past_len U[2048,8191] seeded, d 128, S 8192",
-                                          timing="HIP graph of 20 calls replayed 20 times, per call")
+        extra["wide_group_decode"] = dict(
+            wide, context="past_len U[2048,8191] seeded, d 128, S 8192",
+            timing="HIP graph of 20 calls replayed 20 times, per call (partials + combine); wide_kernel_us, kv_gbs "
+                   "and split_k_us: each call on the next of cache_layers cache pairs (cold, as across the layers "
+                   "of a step); warm_*: every call on the same cache pair (rows partly held in the MALL)")
     if not args.no_extra:
         del flush
         torch.cuda.empty_cache()

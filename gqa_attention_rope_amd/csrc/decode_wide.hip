@@ -135,8 +135,13 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
 #pragma unroll
         for (int x = 0; x < HALF; ++x) {
             const uint32_t dst = lds_base + (uint32_t)((x * WD_THREADS + wave * 64) * 16);
-            load_lds16(rk, dst + (uint32_t)(buf * TILEB), dma_off[x], soff);
-            load_lds16(rv, dst + (uint32_t)((2 + buf) * TILEB), dma_off[x], soff);
+            if (HB == 2) {  // non-temporal: each row is read once per launch
+                load_lds16_nt(rk, dst + (uint32_t)(buf * TILEB), dma_off[x], soff);
+                load_lds16_nt(rv, dst + (uint32_t)((2 + buf) * TILEB), dma_off[x], soff);
+            } else {
+                load_lds16(rk, dst + (uint32_t)(buf * TILEB), dma_off[x], soff);
+                load_lds16(rv, dst + (uint32_t)((2 + buf) * TILEB), dma_off[x], soff);
+            }
         }
     };
     if (t0 < t1) load_tile(t0, 0);
@@ -282,8 +287,11 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
 
 // Merge the records of one (sequence, query head) in order: M = max m,
 // out = sum o e^(m - M) / (sum l e^(m - M) [+ e^(sink - M)]).  One wave; lane r
-// holds record r's (m, l), and the outputs are read eight records at a time.
-template <int D>
+// holds record r's (m, l).  Every load is issued before the first use: the
+// (m, l) pairs and the output slices of records 0 .. NR-1 (NR >= nrec; the
+// records past nrec re-read the last one and get weight zero), so the merge
+// waits on memory once.
+template <int D, int NR>
 __global__ __launch_bounds__(64) void decode_wide_combine_kernel(const float* __restrict__ recs,
                                                                  uint16_t* __restrict__ out, int n_q, int n_kv,
                                                                  int nrec, const float* __restrict__ sink_logits) {
@@ -294,10 +302,17 @@ __global__ __launch_bounds__(64) void decode_wide_combine_kernel(const float* __
     const float* r0p = recs + ((size_t)(b * n_kv + j) * nrec * g + hl) * REC;
     const size_t stride = (size_t)g * REC;
     float m_l = -INFINITY, l_l = 0.f;
-    if (lane < nrec) {  // nrec <= 64
+    if (lane < nrec) {  // nrec <= NR <= 64
         const float2 ml = *reinterpret_cast<const float2*>(r0p + lane * stride);
         m_l = ml.x;
         l_l = ml.y;
+    }
+    float ov[NR][DPL];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const float* rr = r0p + (r < nrec ? r : nrec - 1) * stride + 4 + DPL * lane;
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) ov[r][x] = rr[x];
     }
     const float sk = sink_logits ? sink_logits[h] * WD_LOG2E : -INFINITY;
     const float M = fmaxf(wd_wave_max(m_l), sk);
@@ -306,22 +321,11 @@ __global__ __launch_bounds__(64) void decode_wide_combine_kernel(const float* __
     float acc[DPL];
 #pragma unroll
     for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
-    for (int q0 = 0; q0 < nrec; q0 += 8) {
-        float ov[8][DPL];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int r = q0 + u < nrec ? q0 + u : 0;
-            const float* rr = r0p + r * stride + 4 + DPL * lane;
+    for (int r = 0; r < NR; ++r) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), r));
 #pragma unroll
-            for (int x = 0; x < DPL; ++x) ov[u][x] = rr[x];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            // q0 + u <= 63 (q0 is a multiple of 8 below nrec <= 64); lanes >= nrec hold 0
-            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), q0 + u));
-#pragma unroll
-            for (int x = 0; x < DPL; ++x) acc[x] += w * ov[u][x];
-        }
+        for (int x = 0; x < DPL; ++x) acc[x] += w * ov[r][x];
     }
     const float inv = 1.f / lsum;
     uint16_t* dst = out + (size_t)(b * n_q + h) * D;
@@ -329,6 +333,22 @@ __global__ __launch_bounds__(64) void decode_wide_combine_kernel(const float* __
         *reinterpret_cast<uint32_t*>(dst + 2 * lane) = cvt_pk_bf16(acc[0] * inv, acc[DPL - 1] * inv);
     else
         dst[lane] = (uint16_t)(cvt_pk_bf16(acc[0] * inv, 0.f) & 0xffffu);
+}
+
+template <int D>
+hipError_t launch_wide_combine(const float* recs, uint16_t* out, int n_q, int n_kv, int nb, int nrec,
+                               const float* sink_logits, hipStream_t st) {
+    const dim3 grid(n_q, nb);
+    if (nrec <= 16)
+        hipLaunchKernelGGL((decode_wide_combine_kernel<D, 16>), grid, dim3(64), 0, st, recs, out, n_q, n_kv, nrec,
+                           sink_logits);
+    else if (nrec <= 32)
+        hipLaunchKernelGGL((decode_wide_combine_kernel<D, 32>), grid, dim3(64), 0, st, recs, out, n_q, n_kv, nrec,
+                           sink_logits);
+    else
+        hipLaunchKernelGGL((decode_wide_combine_kernel<D, 64>), grid, dim3(64), 0, st, recs, out, n_q, n_kv, nrec,
+                           sink_logits);
+    return hipGetLastError();
 }
 
 using wide_fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int, float*, int, int, int,
@@ -402,14 +422,11 @@ hipError_t launch_decode_wide(const uint16_t* q_rot, const uint16_t* k_cache, co
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         prof_begin(K_DECODE_COMBINE, st);
-        if (d == 128)
-            hipLaunchKernelGGL(decode_wide_combine_kernel<128>, dim3(n_q, nb), dim3(64), 0, st, recs,
-                               out + (size_t)b0 * n_q * d, n_q, n_kv, nsplit * rg, sink_logits);
-        else
-            hipLaunchKernelGGL(decode_wide_combine_kernel<64>, dim3(n_q, nb), dim3(64), 0, st, recs,
-                               out + (size_t)b0 * n_q * d, n_q, n_kv, nsplit * rg, sink_logits);
+        e = d == 128 ? launch_wide_combine<128>(recs, out + (size_t)b0 * n_q * d, n_q, n_kv, nb, nsplit * rg,
+                                                sink_logits, st)
+                     : launch_wide_combine<64>(recs, out + (size_t)b0 * n_q * d, n_q, n_kv, nb, nsplit * rg,
+                                               sink_logits, st);
         prof_end(K_DECODE_COMBINE, st);
-        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

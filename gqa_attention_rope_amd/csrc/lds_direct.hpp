@@ -24,6 +24,11 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t
     asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
                  : "memory");
 }
+// The same with the non-temporal cache policy, for data read once per launch.
+__device__ __forceinline__ void load_lds16_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voff, int soff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
+}
 
 // Transposing read of 4 bf16 per lane: within each group of 16 lanes, lanes
 // 4i .. 4i+3 name row i (4 consecutive values each, 16 in all) and lane n
