@@ -18,8 +18,9 @@
 // How:
 //  * Grid (split, KV head j, sequence b), 4 waves.  A segment's tiles (64 rows;
 //    sink and window tiles only, under a window) are cut into nsplit
-//    contiguous ranges.  Wave w owns head block hb = w % HB (16 heads) and row
-//    group w / HB of each tile (RG = 4 / HB groups of 64 / RG rows).
+//    contiguous ranges.  Wave w owns head block hb = w % HB (16 heads; HB = 1,
+//    2 or 4 blocks for g <= 16, 32, 64) and row group w / HB of each tile
+//    (RG = 4 / HB groups of 64 / RG rows).
 //  * A tile's K and V rows go from HBM straight into LDS (range-checked
 //    buffer loads with the LDS destination), row-major with an XOR swizzle of
 //    the 16-byte pieces: the MFMA A operand reads of K (16 rows of one piece)
@@ -32,10 +33,13 @@
 //    O += P V when the 32 rows of a K-step are taken in that order, so P never
 //    leaves the registers.  P enters as a bf16 high part plus a bf16
 //    remainder (two MFMAs, about 16 significant bits); V's B operand follows
-//    the same row order (two transposed 8-byte reads per lane).
+//    the same row order (two transposed 8-byte reads per lane).  With 16 rows
+//    per wave (g <= 16) the k-step is those 16 rows, on
+//    v_mfma_f32_16x16x16_bf16 with one transposed read.
 //  * Online softmax per head (two lane shuffles per reduction); the output
 //    rescale fetches each head's factor from the lanes that own it.
-//  * Each (split, row group) writes one (max, sum, unnormalised output)
+//  * The row groups of a head block merge their (max, sum, unnormalised
+//    output) states through LDS in row-group order, and each split writes one
 //    record per head.  The split count keeps every segment's records (all
 //    heads of all splits) within 2048, which bounds the record traffic for
 //    large g against the parallelism that more splits buy.  A second kernel merges the
@@ -78,7 +82,7 @@ __device__ __forceinline__ float wd_wave_reduce(float v) {
 __device__ __forceinline__ float wd_wave_max(float v) { return wd_wave_reduce<true>(v); }
 __device__ __forceinline__ float wd_wave_sum(float v) { return wd_wave_reduce<false>(v); }
 
-// D head size; HB blocks of 16 heads (g <= 16 HB), HB in {2, 4}
+// D head size; HB blocks of 16 heads (g <= 16 HB), HB in {1, 2, 4}
 template <int D, int HB>
 __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -89,12 +93,11 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
     constexpr int TILEB = WD_TILE * ROWB;            // bytes of one tensor's tile
     constexpr int HALF = TILEB / (16 * WD_THREADS);  // 16-byte loads per thread per tensor
     constexpr int RG = 4 / HB;                       // row groups
-    constexpr int ROWS_W = WD_TILE / RG;             // rows of a tile per wave (32 or 64)
+    constexpr int ROWS_W = WD_TILE / RG;             // rows of a tile per wave (16, 32 or 64)
     constexpr int KB = ROWS_W / 16;                  // 16-row blocks per wave
     constexpr int KS = D / 32;                       // MFMA k-steps over the head dim
     constexpr int DB = D / 16;                       // 16-dim blocks of the output
     constexpr int REC = D + 4;
-    constexpr int NREC = RG;                         // records per split and head
 
     // K buffers 0 and 1, then V buffers 0 and 1
     __shared__ __align__(16) unsigned char smem[4 * TILEB];
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
 #pragma unroll
         for (int x = 0; x < HALF; ++x) {
             const uint32_t dst = lds_base + (uint32_t)((x * WD_THREADS + wave * 64) * 16);
-            if (HB == 2) {  // non-temporal: each row is read once per launch
+            if (HB <= 2) {  // non-temporal: each row is read once per launch
                 load_lds16_nt(rk, dst + (uint32_t)(buf * TILEB), dma_off[x], soff);
                 load_lds16_nt(rv, dst + (uint32_t)((2 + buf) * TILEB), dma_off[x], soff);
             } else {
@@ -243,37 +246,102 @@ __global__ __launch_bounds__(WD_THREADS, 2) void decode_wide_kernel(
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db][e] *= a;
         }
-        // O += P V, 32 rows per k-step: k index 8 lq + e <-> row 16 (2 kk) + 4 lq + e (e < 4),
-        // row 16 (2 kk + 1) + 4 lq + e - 4 (e >= 4), the order the score registers already have
-#pragma unroll
-        for (int kk = 0; kk < KB / 2; ++kk) {
-            const f32x4_t p0 = sacc[2 * kk], p1 = sacc[2 * kk + 1];
+        if constexpr (KB == 1) {
+            // O += P V over the wave's 16 rows in one k-step: k index 4 lq + e <-> row 4 lq + e
+            const f32x4_t p0 = sacc[0];
             const uint32_t h0 = cvt_pk_bf16(p0[0], p0[1]), h1 = cvt_pk_bf16(p0[2], p0[3]);
-            const uint32_t h2 = cvt_pk_bf16(p1[0], p1[1]), h3 = cvt_pk_bf16(p1[2], p1[3]);
-            const u32x4_t hi = {h0, h1, h2, h3};
-            const u32x4_t lo = {cvt_pk_bf16(p0[0] - bf_lo(h0), p0[1] - bf_hi(h0)),
-                                cvt_pk_bf16(p0[2] - bf_lo(h1), p0[3] - bf_hi(h1)),
-                                cvt_pk_bf16(p1[0] - bf_lo(h2), p1[1] - bf_hi(h2)),
-                                cvt_pk_bf16(p1[2] - bf_lo(h3), p1[3] - bf_hi(h3))};
-            const int r0 = rg * ROWS_W + 32 * kk + 4 * lq;
+            const i16x4_t hi = __builtin_bit_cast(i16x4_t, make_uint2(h0, h1));
+            const i16x4_t lo = __builtin_bit_cast(
+                i16x4_t, make_uint2(cvt_pk_bf16(p0[0] - bf_lo(h0), p0[1] - bf_hi(h0)),
+                                    cvt_pk_bf16(p0[2] - bf_lo(h1), p0[3] - bf_hi(h1))));
+            const int r0 = rg * ROWS_W;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const i16x4_t a = read_tr16(s_v + v_rd[db] + (r0 - 4 * lq) * ROWB);
-                const i16x4_t c = read_tr16(s_v + v_rd[db] + (r0 - 4 * lq + 16) * ROWB);
-                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), bop, oacc[db], 0,
-                                                                    0, 0);
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), bop, oacc[db], 0,
-                                                                    0, 0);
+                const i16x4_t bop = read_tr16(s_v + v_rd[db] + r0 * ROWB);
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, bop, oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, bop, oacc[db], 0, 0, 0);
+            }
+        } else {
+            // O += P V, 32 rows per k-step: k index 8 lq + e <-> row 16 (2 kk) + 4 lq + e (e < 4),
+            // row 16 (2 kk + 1) + 4 lq + e - 4 (e >= 4), the order the score registers already have
+    #pragma unroll
+            for (int kk = 0; kk < KB / 2; ++kk) {
+                const f32x4_t p0 = sacc[2 * kk], p1 = sacc[2 * kk + 1];
+                const uint32_t h0 = cvt_pk_bf16(p0[0], p0[1]), h1 = cvt_pk_bf16(p0[2], p0[3]);
+                const uint32_t h2 = cvt_pk_bf16(p1[0], p1[1]), h3 = cvt_pk_bf16(p1[2], p1[3]);
+                const u32x4_t hi = {h0, h1, h2, h3};
+                const u32x4_t lo = {cvt_pk_bf16(p0[0] - bf_lo(h0), p0[1] - bf_hi(h0)),
+                                    cvt_pk_bf16(p0[2] - bf_lo(h1), p0[3] - bf_hi(h1)),
+                                    cvt_pk_bf16(p1[0] - bf_lo(h2), p1[1] - bf_hi(h2)),
+                                    cvt_pk_bf16(p1[2] - bf_lo(h3), p1[3] - bf_hi(h3))};
+                const int r0 = rg * ROWS_W + 32 * kk + 4 * lq;
+    #pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const i16x4_t a = read_tr16(s_v + v_rd[db] + (r0 - 4 * lq) * ROWB);
+                    const i16x4_t c = read_tr16(s_v + v_rd[db] + (r0 - 4 * lq + 16) * ROWB);
+                    const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), bop, oacc[db], 0,
+                                                                        0, 0);
+                    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), bop, oacc[db], 0,
+                                                                        0, 0);
+                }
             }
         }
     }
 
-    // ---- records of this (split, row group): (m, l, pad, pad, o[D]) per head
+    // ---- record of this split: (m, l, pad, pad, o[D]) per head
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     const size_t segi = (size_t)b * n_kv + j;
-    float* rbase = recs + ((segi * nsplit + sp) * NREC + rg) * g * REC;
+    float* rbase = recs + (segi * nsplit + sp) * g * REC;
+    if constexpr (RG > 1) {
+        // Row groups merge in order through LDS (the tile buffers, free once
+        // every wave is past its last tile): M = max m, l = sum l e^(m - M),
+        // o = sum o e^(m - M); row group 0 of each head block writes the record.
+        constexpr int NH = 16 * HB;  // heads of the workgroup
+        float* s_o = reinterpret_cast<float*>(smem);                           // [RG][NH][D]
+        float2* s_ml = reinterpret_cast<float2*>(s_o + (size_t)RG * NH * D);  // [RG][NH]
+        static_assert((size_t)RG * NH * (D * 4 + 8) <= sizeof(smem), "merge state fits the tile buffers");
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                s_o[((size_t)rg * NH + 16 * hb + 4 * lq + e) * D + 16 * db + l16] = oacc[db][e];
+        if (lq == 0) s_ml[rg * NH + 16 * hb + l16] = make_float2(m_run, l_run);
+        __syncthreads();
+        if (rg != 0) return;
+        {
+            float M = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) M = fmaxf(M, s_ml[r * NH + hq].x);
+            float L = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const float2 ml = s_ml[r * NH + hq];
+                L += ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M) * ml.y;
+            }
+            m_run = M;
+            l_run = L;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hw = 16 * hb + 4 * lq + e;  // this lane's output head
+            float M = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) M = fmaxf(M, s_ml[r * NH + hw].x);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db][e] = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const float mr = s_ml[r * NH + hw].x;
+                const float w = mr == -INFINITY ? 0.f : fast_exp2(mr - M);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db][e] += w * s_o[((size_t)r * NH + hw) * D + 16 * db + l16];
+            }
+        }
+    }
     if (lq == 0 && hq < g) *reinterpret_cast<float2*>(rbase + (size_t)hq * REC) = make_float2(m_run, l_run);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -298,7 +366,7 @@ __global__ __launch_bounds__(64) void decode_wide_combine_kernel(const float* __
     constexpr int REC = D + 4, DPL = D / 64;
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int g = n_q / n_kv, j = h / g, hl = h % g;
-    // record r of head hl: recs + ((segment * nrec + r) * g + hl) * REC, records ordered by (split, row group)
+    // record r of head hl: recs + ((segment * nrec + r) * g + hl) * REC, one record per split, in split order
     const float* r0p = recs + ((size_t)(b * n_kv + j) * nrec * g + hl) * REC;
     const size_t stride = (size_t)g * REC;
     float m_l = -INFINITY, l_l = 0.f;
@@ -378,8 +446,7 @@ int decode_wide_splits(int nb, int n_kv, int g, int max_past_len, int window, in
     const long long segs = (long long)nb * n_kv;
     const long long target = wg_override > 0 ? wg_override : 2LL * cu_count;
     long long n = (target + segs - 1) / segs;
-    const int rg = g <= 32 ? 2 : 1;
-    const long long cap = WD_MAX_SEG_RECORDS / (rg * g);
+    const long long cap = WD_MAX_SEG_RECORDS / g;  // one record per head and split
     if (n > cap) n = cap;
     if (n > tiles) n = tiles;
     if (n > DECODE_WIDE_MAX_SPLITS) n = DECODE_WIDE_MAX_SPLITS;
@@ -389,11 +456,10 @@ int decode_wide_splits(int nb, int n_kv, int g, int max_past_len, int window, in
 size_t decode_wide_record_bytes(int B, int n_q, int n_kv, int d) {
     int nb = DECODE_WIDE_MAX_SEGS / n_kv;
     if (nb > B) nb = B;
-    // records per segment: rg row groups x g heads per split, at most
-    // DECODE_WIDE_MAX_SPLITS splits and at most WD_MAX_SEG_RECORDS in all
+    // records per segment: g heads per split, at most DECODE_WIDE_MAX_SPLITS
+    // splits and at most WD_MAX_SEG_RECORDS in all
     const int g = n_q / n_kv;
-    const long long per_split = (long long)(g <= 32 ? 2 : 1) * g;
-    long long recs = per_split * DECODE_WIDE_MAX_SPLITS;
+    long long recs = (long long)g * DECODE_WIDE_MAX_SPLITS;
     if (recs > WD_MAX_SEG_RECORDS) recs = WD_MAX_SEG_RECORDS;
     return (size_t)nb * n_kv * (size_t)recs * (d + 4) * sizeof(float);
 }
@@ -403,13 +469,12 @@ hipError_t launch_decode_wide(const uint16_t* q_rot, const uint16_t* k_cache, co
                               int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
                               int wg_override, hipStream_t st) {
     const int g = n_q / n_kv;
-    const int rg = g <= 32 ? 2 : 1;
     float* recs = ws + DECODE_WS_HEADER_FLOATS;
     wide_fn fn;
     if (d == 128)
-        fn = g <= 32 ? decode_wide_kernel<128, 2> : decode_wide_kernel<128, 4>;
+        fn = g <= 16 ? decode_wide_kernel<128, 1> : g <= 32 ? decode_wide_kernel<128, 2> : decode_wide_kernel<128, 4>;
     else
-        fn = g <= 32 ? decode_wide_kernel<64, 2> : decode_wide_kernel<64, 4>;
+        fn = g <= 16 ? decode_wide_kernel<64, 1> : g <= 32 ? decode_wide_kernel<64, 2> : decode_wide_kernel<64, 4>;
     const int per = DECODE_WIDE_MAX_SEGS / n_kv;  // sequences per launch (bounds the record space)
     for (int b0 = 0; b0 < B; b0 += per) {
         const int nb = (B - b0) < per ? (B - b0) : per;
@@ -422,10 +487,9 @@ hipError_t launch_decode_wide(const uint16_t* q_rot, const uint16_t* k_cache, co
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         prof_begin(K_DECODE_COMBINE, st);
-        e = d == 128 ? launch_wide_combine<128>(recs, out + (size_t)b0 * n_q * d, n_q, n_kv, nb, nsplit * rg,
-                                                sink_logits, st)
-                     : launch_wide_combine<64>(recs, out + (size_t)b0 * n_q * d, n_q, n_kv, nb, nsplit * rg,
-                                               sink_logits, st);
+        e = d == 128 ? launch_wide_combine<128>(recs, out + (size_t)b0 * n_q * d, n_q, n_kv, nb, nsplit, sink_logits,
+                                                st)
+                     : launch_wide_combine<64>(recs, out + (size_t)b0 * n_q * d, n_q, n_kv, nb, nsplit, sink_logits, st);
         prof_end(K_DECODE_COMBINE, st);
         if (e != hipSuccess) return e;
     }

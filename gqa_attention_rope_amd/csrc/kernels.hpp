@@ -103,7 +103,7 @@ constexpr int DECODE_WS_HEADER_FLOATS = 64;
 constexpr int DECODE_WIDE_MIN_G = 16;       // used from this group size on
 constexpr int DECODE_WIDE_MAX_G = 64;
 constexpr int DECODE_WIDE_MAX_SEGS = 64;    // segments per launch (bounds the record space)
-constexpr int DECODE_WIDE_MAX_SPLITS = 32;  // splits per segment
+constexpr int DECODE_WIDE_MAX_SPLITS = 64;  // splits per segment (the wide combine merges at most 64 records)
 int decode_wide_splits(int nb, int n_kv, int g, int max_past_len, int window, int n_sink, int wg_override);
 size_t decode_wide_record_bytes(int B, int n_q, int n_kv, int d);
 // Smallest group size that takes the wide kernel (0 restores the default).

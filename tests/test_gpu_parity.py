@@ -745,8 +745,8 @@ WIDE_CASES = [
     (2, 34, 2, 128, 500, [499, 130], 5.0e5, "interleaved", None),             # g = 17
     (4, 48, 2, 64, 400, [399, 1, 64, 250], 1.0e4, "interleaved", None),       # g = 24
     (9, 256, 8, 128, 200, [199, 3, 64, 100, 150, 7, 63, 128, 77], 5.0e5, "interleaved", None),  # two launch slices
-    (2, 16, 1, 128, 4200, [4100, 2100], 5.0e5, "interleaved", None),          # g = 16: 32 splits x 2 row groups,
-    (2, 16, 1, 128, 1100, [1087, 500], 5.0e5, "half", None),                  # 64 and 34 records per head merged
+    (2, 16, 1, 128, 4200, [4100, 2100], 5.0e5, "interleaved", None),          # g = 16: 64 and 17 splits, so 64
+    (2, 16, 1, 128, 1100, [1087, 500], 5.0e5, "half", None),                  # and 17 records per head merged
 ]
 
 
