@@ -102,7 +102,8 @@ def parse():
                     help="first run one plain device copy of this many GiB (reference for HBM byte counters)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling leg")
     ap.add_argument("--legs", default="prefill,long,small,wide",
-                    help="extra legs to run (comma list of prefill, long, small, wide)")
+                    help="extra legs to run (comma list of prefill, long, small, wide, batch; batch is the decode "
+                         "attention batch-size sweep, not run by default)")
     return ap.parse_args()
 
 
@@ -347,6 +348,43 @@ def wide_group_workload(gq, synth, dev, B, n_q, n_kv, seed, cold_bytes=6.4e8):
     return warm, cold, kvb, layers
 
 
+BATCH_SWEEP = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def batch_sweep_workload(gq, synth, dev, B, cold_bytes=1.2e9):
+    """gqa_decode_attn at the headline's shape (32/8 heads, d 128, S 8192, past_len U[512, 8191], seed 1003) for
+    batch size B, each call on the next of enough cache pairs that about cold_bytes of K/V lie between two reads
+    of the same rows.  Returns (call, kv bytes per call, cache pairs)."""
+    import math
+    import torch
+    w = synth.WORKLOADS[HEADLINE]
+    n_q, n_kv, d, S = w["n_q"], w["n_kv"], w["d"], w["S"]
+    past = synth.past_lengths(B, w["past"], w["seed"])
+    kvb = kv_bytes(past, n_kv, d)
+    layers = min(32, max(2, math.ceil(cold_bytes / kvb)))
+    kcs, vcs = [], []
+    for l in range(layers):
+        kc = torch.empty((B, n_kv, S, d), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        synth.fill_normal_bf16_(kc, 7000 + 2 * l)
+        synth.fill_normal_bf16_(vc, 7001 + 2 * l)
+        kcs.append(kc)
+        vcs.append(vc)
+    q = synth.normal_bf16((B, n_q, 1, d), w["seed"] + 11, dev)
+    pl = torch.as_tensor(past, device=dev)
+    maxp = int(past.max())
+    out = torch.empty_like(q)
+    ws = torch.zeros(gq.gqa_decode_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=dev)
+    nxt = [0]
+
+    def call():
+        l = nxt[0] % layers
+        nxt[0] += 1
+        gq.gqa_decode_attn(q, kcs[l], vcs[l], pl, maxp, out=out, workspace=ws)
+
+    return call, kvb, layers
+
+
 def cpu_baseline(info, kc, vc, q, kn, vn):
     """The fp64 oracle on one layer of the headline step (all 32 sequences), with every host core this process
     may use and with one thread."""
@@ -550,6 +588,21 @@ def main():
             timing="HIP graph of 20 calls replayed 20 times, per call (partials + combine); wide_kernel_us, kv_gbs "
                    "and split_k_us: each call on the next of cache_layers cache pairs (cold, as across the layers "
                    "of a step); warm_*: every call on the same cache pair (rows partly held in the MALL)")
+    if not args.no_extra and "batch" in legs:
+        sweep = {}
+        for Bs in BATCH_SWEEP:
+            call, kvb, layers = batch_sweep_workload(gq, synth, dev, Bs)
+            t = graph_us(call)
+            sweep[f"B{Bs}"] = {"us": round(t, 2), "kv_gbs": round(kvb / (t * 1e-6) / 1e9, 1),
+                               "frac_hbm_peak": round(kvb / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "kv_bytes": kvb,
+                               "cache_layers": layers}
+            del call
+            torch.cuda.empty_cache()
+        extra["decode_batch_sweep"] = dict(
+            sweep, context="gqa_decode_attn (partials + combine), 32/8 heads, d 128, S 8192, past_len U[512,8191] "
+                           "seed 1003 (the headline's), batch size B",
+            timing="HIP graph of 20 calls replayed 20 times, per call, each call on the next of cache_layers cache "
+                   "pairs (cold)")
     if not args.no_extra:
         del flush
         torch.cuda.empty_cache()
