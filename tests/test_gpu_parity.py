@@ -884,6 +884,21 @@ def test_prefill_wide_groups(case):
     check_out(synth.bits(out), ref, "prefill, wide group")
 
 
+def test_wide_group_decode_g16_window_learned_sinks():
+    """The one-head-block path (g = 16: 16 rows per wave, row groups merged in the workgroup) under a window
+    with sinks and learned sink logits; tiles no query sees hold NaN."""
+    B, n_q, n_kv, d, S, past, W, NS = 3, 32, 2, 128, 3000, [2999, 700, 40], 300, 4
+    say("wide decode g16 window")
+    q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=2301)
+    sinks = np.random.default_rng(11).standard_normal(n_q).astype(np.float32)
+    ref = attend(q, kc, vc, past, n_kv, window=W, n_sink=NS, sink_logits=sinks)
+    assert poison_unread_tiles((kc, vc), past, W, NS) > 0
+    out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), window=W, n_sink=NS,
+                             sink_logits=torch.from_numpy(sinks).to(DEV))
+    torch.cuda.synchronize()
+    check_out(synth.bits(out), ref, "wide decode, g 16, window")
+
+
 def test_wide_group_decode_d64_window():
     B, n_q, n_kv, d, S, past, W, NS = 3, 32, 1, 64, 2000, [1999, 40, 1000], 300, 2
     say("wide decode d64 window")
