@@ -432,7 +432,7 @@ int gqa_set_decode_slot_ratio(int ratio_permille) {
 
 int gqa_set_decode_schedule(int static_permille, int chunk_tiles) {
     if (static_permille < 0 && chunk_tiles <= 0) {
-        gqa::set_decode_schedule(gqa::DECODE_DEFAULT_STATIC_PM, gqa::DECODE_DEFAULT_CHUNK);
+        gqa::set_decode_schedule(-1, gqa::DECODE_DEFAULT_CHUNK);  // static fraction chosen per launch
         return GQA_OK;
     }
     if (static_permille < 0 || static_permille > 1000 || chunk_tiles < 1) return GQA_ERR_INVALID_ARG;

@@ -347,7 +347,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     int ld_rid = w;
     if (ld_left > 0) ld = cursor_at(tau_w);
     int nx_tau = 0, nx_len = 0, nx_rid = 0;
-    bool have_next = false, no_more = false, pending = false;
+    bool have_next = false, no_more = sc.n_dyn == 0, pending = false;  // no chunks: no ticket is ever taken
     auto take_ticket = [&] __attribute__((always_inline)) (int t) {
         if (t >= 0 && t < sc.n_dyn) {  // (a counter left non-zero by a broken caller only loses work)
             have_next = true;
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
         }
     };
     // a short share needs the first chunk before the pipeline is primed
-    if (ld_left <= 2) {
+    if (ld_left <= 2 && !no_more) {
         if (tid == 0) s_ticket = atomicAdd(ticket_ctr, 1);
         __syncthreads();
         take_ticket(uni(s_ticket));
@@ -882,7 +882,7 @@ const Variant& pick_variant(int g) {
     return kVariants[sizeof(kVariants) / sizeof(kVariants[0]) - 1];
 }
 
-int g_static_pm = DECODE_DEFAULT_STATIC_PM;
+int g_static_pm = -1;  // -1: chosen per launch (see launch_decode)
 int g_chunk = DECODE_DEFAULT_CHUNK;
 int g_slot_ratio_pm = 0;  // 0: the kernel variant's default
 
@@ -1022,6 +1022,7 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
     }
     // never more workgroups than tiles: a small problem would otherwise have
     // most workgroups queue on the ticket counter with nothing to do
+    long long tiles_bound;  // tiles of one launch with every past_len at max_past_len
     {
         long long per_seg = (max_past_len + 1 + TILE - 1) / TILE;
         if (window > 0) {
@@ -1029,13 +1030,21 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
             if (wt < per_seg) per_seg = wt;
         }
         const long long bs = B < DECODE_MAX_B ? B : DECODE_MAX_B;
-        const long long tiles = bs * n_kv * p.nhc * per_seg;
-        if (G > tiles) G = (int)tiles;
+        tiles_bound = bs * n_kv * p.nhc * per_seg;
+        if (G > tiles_bound) G = (int)tiles_bound;
     }
     if (G > DECODE_MAX_WG) G = DECODE_MAX_WG;
     if (G < 1) G = 1;
     const float scale_log2 = scale * LOG2E;
-    const int spm = g_static_pm;
+    // Default schedule: with at most DECODE_STATIC_ONLY_TILES tiles per
+    // workgroup (small batches) every tile goes into a static share.  There the
+    // slot-weighted shares already balance the workgroups, and a dynamic tail
+    // only adds ticket round trips ahead of the first loads and more records
+    // (measured: B4 30.1 -> 23.9 us, B16 59.7 -> 57.3 us at contexts up to
+    // 8192); with many tiles per workgroup the tail absorbs the spread
+    // between workgroups (the 70B shape is 1.2 % faster with it).
+    const int spm = g_static_pm >= 0 ? g_static_pm
+                  : (tiles_bound <= (long long)DECODE_STATIC_ONLY_TILES * G ? 1000 : DECODE_DEFAULT_STATIC_PM);
     const Shares shares = make_shares(G, cu_count, g_slot_ratio_pm > 0 ? g_slot_ratio_pm : default_slot_ratio(v));
     int4* const dir = reinterpret_cast<int4*>(ws + HDR_FLOATS);
     float* const recs = ws + HDR_FLOATS + 8 * split_segments(B, n_q, n_kv, d);

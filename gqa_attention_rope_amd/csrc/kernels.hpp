@@ -51,6 +51,9 @@ constexpr int DECODE_MAX_WG = 2048;
 // chunk grows when a launch would need more).
 constexpr int DECODE_DEFAULT_STATIC_PM = 900;
 constexpr int DECODE_DEFAULT_CHUNK = 3;
+// ... unless a launch has at most this many tiles per workgroup (bounded with
+// every past_len at max_past_len): then every tile is in a static share.
+constexpr int DECODE_STATIC_ONLY_TILES = 32;
 constexpr int DECODE_MAX_CHUNKS = 8192;
 // The static shares are weighted by dispatch slot (the k-th workgroup resident
 // on a CU): each slot's share is a fixed multiple of the next younger one's,
