@@ -192,6 +192,35 @@ def stream_ceiling(gq, dev, nbytes):
             "timing": "HIP events around each launch, mean of 20 launches"}
 
 
+def mfma_ceiling(gq, dev, workgroups=512, iters=4000):
+    """Sustained rate of the prefill kernel's matrix instruction (bf16 16x16x32 MFMA, 16384 flops) with every
+    CU busy, from the library's matrix-rate probe at the prefill's occupancy (two 4-wave workgroups per CU),
+    and the shader clock the probe recorded.  The measured counterpart of the datasheet peak, as the
+    streaming-read ceiling is for HBM."""
+    import torch
+    sink = torch.zeros(8 * workgroups, dtype=torch.int64, device=dev)
+    gq.gqa_measure_mfma_rate(workgroups, max(1, iters // 4), sink)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        gq.gqa_measure_mfma_rate(workgroups, iters, sink)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3
+        w = sink.view(-1, 8).to(torch.float64).cpu()
+        mhz = float(w[:, 4].sum() / w[:, 5].sum() * 100.0)
+        if best is None or us < best[0]:
+            best = (us, mhz)
+    us, mhz = best
+    flops = workgroups * 4 * iters * 8 * 16384
+    tf = flops / (us * 1e-6) / 1e12
+    return {"tflops": round(tf, 1), "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "clock_mhz": round(mhz),
+            "instruction": "v_mfma_f32_16x16x32_bf16, random operands", "workgroups": workgroups,
+            "timing": "HIP events around one launch (best of 3)"}
+
+
 def decode_workload(gq, synth, name, dev):
     import torch
     w = synth.WORKLOADS[name]
@@ -528,13 +557,16 @@ def main():
         pavg, _ = kernel_avg(gq, pstep, 10, "prefill")
         p_warm, _ = call_kernel_us(gq, pstep, 20)
         p_cold, _ = call_kernel_us(gq, pstep, 20, flush)
+        ceil = mfma_ceiling(gq, dev)
         extra["chunked_prefill"] = {"workload": "llama8b_chunked_prefill B4 T512 P2048", "ms": round(pms, 4),
                                     "tflops": round(flops / (pms * 1e-3) / 1e12, 1),
                                     "kernel_tflops": round(flops / (pavg * 1e-3) / 1e12, 1),
                                     "frac_mfma_peak": round(flops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                     "visible_pair_gflop": round(flops / 1e9, 2),
                                     "kernel_us_warm": p_warm, "kernel_us_cold": p_cold,
-                                    "cold_tflops": round(flops / (p_cold * 1e-6) / 1e12, 1)}
+                                    "cold_tflops": round(flops / (p_cold * 1e-6) / 1e12, 1),
+                                    "mfma_ceiling": ceil,
+                                    "frac_measured_ceiling": round(flops / (pavg * 1e-3) / 1e12 / ceil["tflops"], 4)}
         del pstep
         torch.cuda.empty_cache()
     if not args.no_extra and "long" in legs:

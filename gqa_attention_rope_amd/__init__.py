@@ -41,6 +41,7 @@ EXPORTED = (
     "gqa_decode_step",
     "gqa_status_string",
     "gqa_measure_stream_read",
+    "gqa_measure_mfma_rate",
     "gqa_profile_enable",
     "gqa_profile_read",
     "gqa_profile_reset",
@@ -116,6 +117,8 @@ def lib():
     L.gqa_decode_step.restype = i32
     L.gqa_measure_stream_read.argtypes = [vp, sz, vp, i32, vp]
     L.gqa_measure_stream_read.restype = i32
+    L.gqa_measure_mfma_rate.argtypes = [i32, i32, vp, vp]
+    L.gqa_measure_mfma_rate.restype = i32
     L.gqa_status_string.argtypes = [i32]
     L.gqa_status_string.restype = ctypes.c_char_p
     L.gqa_profile_enable.argtypes = [i32]
@@ -394,6 +397,14 @@ def gqa_measure_stream_read(buf, sink, workgroups, stream=None):
     kernel (the HBM read ceiling); ``sink`` is a device int32 tensor of at least ``workgroups`` entries."""
     _check(lib().gqa_measure_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(workgroups),
                                          _stream(stream)))
+
+
+def gqa_measure_mfma_rate(workgroups, iters, sink, stream=None):
+    """Run the library's matrix-rate probe: ``workgroups`` workgroups of 4 waves, each wave issuing
+    ``iters`` x 8 bf16 16x16x32 MFMAs (16384 flops each) on random operands.  ``sink`` is a device int64
+    tensor of at least 8 * workgroups entries; per workgroup, entries 4 and 5 receive wave 0's shader-clock
+    cycles and 100 MHz ticks over its loop."""
+    _check(lib().gqa_measure_mfma_rate(int(workgroups), int(iters), _ptr(sink), _stream(stream)))
 
 
 def gqa_profile_enable(on=True):

@@ -10,6 +10,7 @@
 
 #include "gqa.h"
 #include "kernels.hpp"
+#include "measure.hpp"
 
 // Decode scratch of gqa_decode_attn_noalloc: one copy per GPU, allocated when
 // the code object is loaded and held until the process ends.  In host code
@@ -373,6 +374,17 @@ int gqa_measure_stream_read(const void* buf, size_t bytes, void* sink, int workg
     if (st != GQA_OK) return st;
     hipError_t e = gqa::launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink), workgroups,
                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GQA_OK : hip_status(e);
+}
+
+int gqa_measure_mfma_rate(int workgroups, int iters, void* sink, void* stream) {
+    if (!sink || (reinterpret_cast<uintptr_t>(sink) & 7u) || workgroups < 1 || workgroups > 65535 || iters < 1 ||
+        iters > (1 << 24))
+        return GQA_ERR_INVALID_ARG;
+    int st = ensure_device();
+    if (st != GQA_OK) return st;
+    hipError_t e = gqa::launch_mfma_rate(static_cast<unsigned long long*>(sink), workgroups, iters,
+                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GQA_OK : hip_status(e);
 }
 

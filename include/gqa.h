@@ -334,6 +334,23 @@ int gqa_profile_reset(void);
 int gqa_measure_stream_read(const void* buf, size_t bytes, void* sink, int workgroups, void* stream);
 
 /*
+ * Measurement support: the sustained rate of the prefill kernel's matrix
+ * instruction (v_mfma_f32_16x16x32_bf16, 16 384 flops each), the ceiling a
+ * matrix-bound kernel can reach on this GPU at the clock it holds under a
+ * full matrix load.  Launches `workgroups` workgroups of 4 waves; every wave
+ * issues 8 MFMAs per iteration for `iters` iterations on random operands, so
+ * a launch performs workgroups * 4 * iters * 8 * 16384 flops (time it with
+ * events on `stream`).  `sink` (device, 8-byte aligned, at least
+ * 64 * workgroups bytes) receives, per workgroup, 8 64-bit words: 0..3 the
+ * folded results of its waves, 4 the shader-clock cycles and 5 the 100 MHz
+ * counter ticks of wave 0 over its loop (their ratio times 100 MHz is the
+ * shader clock), 6..7 zero.  It computes nothing of the attention step.
+ * Errors: INVALID_ARG (null or misaligned sink, workgroups outside 1..65535,
+ * iters outside 1..2^24), HIP.
+ */
+int gqa_measure_mfma_rate(int workgroups, int iters, void* sink, void* stream);
+
+/*
  * Launch-shape override for tests and tuning: the number of workgroups the
  * decode split-K kernel uses (0 = the occupancy-derived default).  Values
  * above the library maximum are clamped.  Results do not depend on it beyond

@@ -323,3 +323,21 @@ def test_decode_noalloc_without_device_is_a_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert decode_noalloc() == HIP
+
+
+def test_measure_mfma_rate_checks_on_host():
+    L = gq.lib()
+    sink = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+    assert L.gqa_measure_mfma_rate(0, 10, sink, None) == INV
+    assert L.gqa_measure_mfma_rate(65536, 10, sink, None) == INV
+    assert L.gqa_measure_mfma_rate(8, 0, sink, None) == INV
+    assert L.gqa_measure_mfma_rate(8, (1 << 24) + 1, sink, None) == INV
+    assert L.gqa_measure_mfma_rate(8, 10, None, None) == INV
+    assert L.gqa_measure_mfma_rate(8, 10, ctypes.c_void_p(0x1004), None) == INV  # not 8-byte aligned
+
+
+def test_measure_mfma_rate_without_device_is_a_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert gq.lib().gqa_measure_mfma_rate(8, 10, ctypes.c_void_p(0x1000), None) == HIP

@@ -279,3 +279,25 @@ def test_window_hidden_rows_contribute_nothing():
                              window=W, n_sink=NS)
     torch.cuda.synchronize()
     check_out(synth.bits(out), refs, "decode step window, extreme hidden rows")
+
+
+# ---------------------------------------------------------------- measurement probe
+
+def test_mfma_rate_probe_writes_its_sink_only():
+    """The matrix-rate probe writes 8 words per workgroup and nothing past them: finite folded results, a
+    positive clock count and 100 MHz tick count per workgroup, zeros in the two spare words."""
+    wg, iters = 8, 64
+    say("mfma rate probe")
+    buf = torch.full((8 * wg + 64,), -1, dtype=torch.int64, device=DEV)
+    gq.gqa_measure_mfma_rate(wg, iters, buf)
+    torch.cuda.synchronize()
+    w = buf.cpu().numpy()
+    assert np.all(w[8 * wg:] == -1), "writes past the sink"
+    w = w[:8 * wg].reshape(wg, 8)
+    folded = w[:, :4].astype(np.uint32).view(np.float32)
+    assert np.all(np.isfinite(folded))
+    assert np.all(w[:, 4] > 0) and np.all(w[:, 5] > 0)
+    assert np.all(w[:, 6:] == 0)
+    mhz = w[:, 4].sum() / w[:, 5].sum() * 100.0
+    say(f"  shader clock over the probe loop: {mhz:.0f} MHz")
+    assert 100.0 < mhz < 5000.0
