@@ -362,7 +362,7 @@ int gqa_set_decode_workgroups(int n);
  * Work-schedule override for tests and tuning: static_permille (0..1000) of
  * the decode tiles are split into static shares, the rest into chunks of
  * chunk_tiles (>= 1) tiles handed out dynamically.  (-1, 0) restores the
- * defaults: chunks of 3 tiles, and 900 per mille static, or every tile static
+ * defaults: chunks of 4 tiles, and 900 per mille static, or every tile static
  * when a launch has at most 32 tiles per workgroup with every past_len at
  * max_past_len (small batches).  Results do not depend on it beyond
  * floating-point rounding.
