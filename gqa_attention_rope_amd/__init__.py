@@ -49,6 +49,7 @@ EXPORTED = (
     "gqa_set_decode_schedule",
     "gqa_set_decode_slot_ratio",
     "gqa_set_decode_wide_min_group",
+    "gqa_set_decode_step_split_min_tiles",
 )
 
 KERNEL_KINDS = {"rope_append": 0, "decode_partial": 1, "decode_combine": 2, "prefill": 3, "decode_step": 4,
@@ -135,6 +136,8 @@ def lib():
     L.gqa_set_decode_schedule.restype = i32
     L.gqa_set_decode_slot_ratio.argtypes = [i32]
     L.gqa_set_decode_slot_ratio.restype = i32
+    L.gqa_set_decode_step_split_min_tiles.argtypes = [i32]
+    L.gqa_set_decode_step_split_min_tiles.restype = i32
     _lib = L
     return L
 
@@ -437,6 +440,12 @@ def gqa_set_decode_slot_ratio(ratio_permille=0):
     """Static share of each dispatch slot relative to the next younger one (per mille); 0 = the kernel
     variant's default.  Returns the override in effect (clamped to [250, 8000]; 0 for the defaults)."""
     return int(lib().gqa_set_decode_slot_ratio(int(ratio_permille)))
+
+
+def gqa_set_decode_step_split_min_tiles(tiles=0):
+    """Tile bound from which gqa_decode_step runs as rope_append + split-K decode (0 restores the default, 512;
+    a large value keeps every step in one launch).  Returns the value in effect."""
+    return int(lib().gqa_set_decode_step_split_min_tiles(int(tiles)))
 
 
 def gqa_set_decode_wide_min_group(g=0):

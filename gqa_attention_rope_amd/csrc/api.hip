@@ -315,7 +315,7 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
     hipError_t e = gqa::launch_decode_step(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), past_len, max_past_len,
-        static_cast<uint16_t*>(out), static_cast<uint16_t*>(q_rot), workspace, B, n_q, n_kv, d, S, rd,
+        static_cast<uint16_t*>(out), static_cast<uint16_t*>(q_rot), workspace, workspace_bytes, B, n_q, n_kv, d, S, rd,
         resolve_scale(scale, d), o.window, o.n_sink, o.sink_logits, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GQA_OK : hip_status(e);
 }
@@ -440,6 +440,11 @@ int gqa_set_decode_slot_ratio(int ratio_permille) {
     else r = 0;
     gqa::set_decode_slot_ratio(r);
     return gqa::decode_slot_ratio();
+}
+
+int gqa_set_decode_step_split_min_tiles(int tiles) {
+    gqa::set_decode_step_split_min_tiles(tiles);
+    return gqa::decode_step_split_min_tiles();
 }
 
 int gqa_set_decode_schedule(int static_permille, int chunk_tiles) {

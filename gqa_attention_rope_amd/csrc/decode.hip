@@ -991,10 +991,13 @@ size_t decode_launch_workspace_bytes(int B, int n_q, int n_kv, int d) {
 void set_decode_wide_min_group(int g) { g_wide_min = g > 0 ? g : DECODE_WIDE_MIN_G; }
 int decode_wide_min_group() { return g_wide_min; }
 
+// sched_hdr: where the split-K scheduling header (the ticket counter) lives,
+// when not at the start of ws (the caller keeps it zero at rest); the record
+// directory and the records follow ws's own header either way.
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
                          int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
-                         int wg_override, hipStream_t st) {
+                         int wg_override, hipStream_t st, float* sched_hdr) {
     if (takes_wide(n_q, n_kv))
         return launch_decode_wide(q_rot, k_cache, v_cache, past_len, max_past_len, out, ws, B, n_q, n_kv, d, S, scale,
                                   window, n_sink, sink_logits, wg_override, st);
@@ -1046,6 +1049,7 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
     const int spm = g_static_pm >= 0 ? g_static_pm
                   : (tiles_bound <= (long long)DECODE_STATIC_ONLY_TILES * G ? 1000 : DECODE_DEFAULT_STATIC_PM);
     const Shares shares = make_shares(G, cu_count, g_slot_ratio_pm > 0 ? g_slot_ratio_pm : default_slot_ratio(v));
+    float* const hdr = sched_hdr ? sched_hdr : ws;
     int4* const dir = reinterpret_cast<int4*>(ws + HDR_FLOATS);
     float* const recs = ws + HDR_FLOATS + 8 * split_segments(B, n_q, n_kv, d);
 
@@ -1066,17 +1070,17 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
         if (chunk < need) chunk = need;
 
         prof_begin(K_DECODE_PARTIAL, st);
-        hipError_t e = (d == 128 ? v.fn128 : v.fn64)(G, q, kc, vc, pl, max_past_len, ws, dir, recs, nb, n_q, n_kv, S,
+        hipError_t e = (d == 128 ? v.fn128 : v.fn64)(G, q, kc, vc, pl, max_past_len, hdr, dir, recs, nb, n_q, n_kv, S,
                                                      p.nhc, scale_log2, spm, (int)chunk, window, n_sink, shares, st);
         prof_end(K_DECODE_PARTIAL, st);
         if (e != hipSuccess) return e;
 
         prof_begin(K_DECODE_COMBINE, st);
         if (d == 128)
-            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, dir, recs,
+            hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, hdr, dir, recs,
                                o, n_q, n_kv, p.nhc, p.gc, sink_logits, shares);
         else
-            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, ws, dir, recs,
+            hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(n_q, nb), dim3(64 * CMB_WAVES), 0, st, hdr, dir, recs,
                                o, n_q, n_kv, p.nhc, p.gc, sink_logits, shares);
         prof_end(K_DECODE_COMBINE, st);
         e = hipGetLastError();

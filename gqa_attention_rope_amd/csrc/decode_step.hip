@@ -420,24 +420,71 @@ static bool step_takes_wide_route(int n_q, int n_kv) {
 }
 static size_t step_qrot_bytes(int B, int n_q, int d) { return ((size_t)B * n_q * d * 2 + 255) / 256 * 256; }
 
-size_t decode_step_workspace_bytes(int B, int n_q, int n_kv, int d) {
-    size_t need = step_counter_bytes(B, n_kv) + (size_t)B * n_q * DECODE_STEP_MAX_SPLITS * (d + 4) * sizeof(float);
+// Larger batches run the step as rope_append followed by the split-K decode
+// (partials + combine), which is faster there.  Measured at 32/8 heads, d 128
+// (graph replays, cold caches): at contexts U[512, 8191] the single launch
+// takes 17.7 / 19.8 / 37.3 / 64.3 / 178 us at B = 1 / 2 / 4 / 8 / 32 against
+// 18.8 / 20.1 / 25.3 / 38.0 / 105 us for the two calls; at past_len 1000,
+// 11.9 / 14.7 / 19.6 us at B = 1 / 2 / 4 against 15.1 / 15.5 / 18.4 us.  The
+// crossover sits between 256 and 700 tiles of 64 rows (bounded with every
+// past_len at max_past_len); from DECODE_STEP_SPLIT_MIN_TILES on the step
+// takes the two calls.
+constexpr int DECODE_STEP_SPLIT_MIN_TILES = 512;
+static int g_step_split_min_tiles = DECODE_STEP_SPLIT_MIN_TILES;
+
+static bool step_takes_split_route(int B, int n_kv, int max_past_len, int window, int n_sink) {
+    long long per_seg = (max_past_len + 1 + 63) / 64;
+    if (window > 0) {
+        const long long wt = (n_sink + 63) / 64 + (window + 63) / 64 + 1;
+        if (wt < per_seg) per_seg = wt;
+    }
+    return (long long)B * n_kv * per_seg >= g_step_split_min_tiles;
+}
+
+// Workspace of the step.  The per-segment counters of the single-launch route
+// (one per (sequence, KV head)) start the workspace and are zero at rest; the
+// split route keeps its scheduling header (the ticket counter, also zero at
+// rest) in the first 256 bytes, which every route leaves zero at rest.  All
+// else a call writes (the single-launch records; the rotated q and the records
+// of the wide or split route) sits at the end of the caller's workspace: a
+// call with B sequences touches only the last step_tail_bytes(B) bytes beyond
+// its counters, so a workspace sized for some batch size serves every smaller
+// one, through every route, in any order (were the records placed right after
+// the counters, a small batch's records would overwrite the counters of a
+// larger batch's later call).
+static size_t step_tail_bytes(int B, int n_q, int n_kv, int d) {
+    size_t t = (size_t)B * n_q * DECODE_STEP_MAX_SPLITS * (d + 4) * sizeof(float);  // single launch
     const int g = n_q / n_kv;
     if (g <= DECODE_WIDE_MAX_G && n_kv <= DECODE_WIDE_MAX_SEGS) {  // any threshold may send the shape there
-        const size_t wide = step_counter_bytes(B, n_kv) + step_qrot_bytes(B, n_q, d) +
-                            DECODE_WS_HEADER_FLOATS * sizeof(float) + decode_wide_record_bytes(B, n_q, n_kv, d);
-        if (wide > need) need = wide;
+        const size_t wide = step_qrot_bytes(B, n_q, d) + DECODE_WS_HEADER_FLOATS * sizeof(float) +
+                            decode_wide_record_bytes(B, n_q, n_kv, d);
+        if (wide > t) t = wide;
     }
-    return need;
+    const size_t split = step_qrot_bytes(B, n_q, d) + decode_workspace_bytes(B, n_q, n_kv, d);
+    if (split > t) t = split;
+    return (t + 255) / 256 * 256;
 }
+
+size_t decode_step_workspace_bytes(int B, int n_q, int n_kv, int d) {
+    return step_counter_bytes(B, n_kv) + step_tail_bytes(B, n_q, n_kv, d);
+}
+
+void set_decode_step_split_min_tiles(int tiles) {
+    g_step_split_min_tiles = tiles > 0 ? tiles : DECODE_STEP_SPLIT_MIN_TILES;
+}
+int decode_step_split_min_tiles() { return g_step_split_min_tiles; }
 
 hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
                               uint16_t* v_cache, const int32_t* past_len, int max_past_len, uint16_t* out,
-                              uint16_t* q_rot, void* ws, int B, int n_q, int n_kv, int d, int S, const RopeDev& rope,
-                              float scale, int window, int n_sink, const float* sink_logits, hipStream_t st) {
+                              uint16_t* q_rot, void* ws, size_t ws_bytes, int B, int n_q, int n_kv, int d, int S,
+                              const RopeDev& rope, float scale, int window, int n_sink, const float* sink_logits,
+                              hipStream_t st) {
     const int g = n_q / n_kv;
+    // the tail: the last step_tail_bytes of the workspace, 256-byte aligned
+    // (ws_bytes >= decode_step_workspace_bytes, checked by the caller)
+    const size_t tail_at = (ws_bytes - step_tail_bytes(B, n_q, n_kv, d)) / 256 * 256;
+    char* const base = static_cast<char*>(ws) + tail_at;
     if (step_takes_wide_route(n_q, n_kv)) {
-        char* base = static_cast<char*>(ws) + step_counter_bytes(B, n_kv);
         uint16_t* qr = q_rot ? q_rot : reinterpret_cast<uint16_t*>(base);
         float* wws = reinterpret_cast<float*>(base + step_qrot_bytes(B, n_q, d));
         hipError_t e = launch_rope_append(q, qr, k_new, v_new, k_cache, v_cache, past_len, max_past_len, B, n_q, n_kv,
@@ -446,9 +493,18 @@ hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const ui
         return launch_decode_wide(qr, k_cache, v_cache, past_len, max_past_len, out, wws, B, n_q, n_kv, d, S, scale,
                                   window, n_sink, sink_logits, 0, st);
     }
+    if (step_takes_split_route(B, n_kv, max_past_len, window, n_sink)) {
+        uint16_t* qr = q_rot ? q_rot : reinterpret_cast<uint16_t*>(base);
+        float* sws = reinterpret_cast<float*>(base + step_qrot_bytes(B, n_q, d));
+        hipError_t e = launch_rope_append(q, qr, k_new, v_new, k_cache, v_cache, past_len, max_past_len, B, n_q, n_kv,
+                                          1, d, S, rope, st);
+        if (e != hipSuccess) return e;
+        return launch_decode(qr, k_cache, v_cache, past_len, max_past_len, out, sws, B, n_q, n_kv, d, S, scale, window,
+                             n_sink, sink_logits, 0, st, static_cast<float*>(ws));
+    }
     const int nsplit = decode_step_splits(B, n_kv, max_past_len, window, n_sink);
     int* counters = static_cast<int*>(ws);
-    float* recs = reinterpret_cast<float*>(static_cast<char*>(ws) + step_counter_bytes(B, n_kv));
+    float* recs = reinterpret_cast<float*>(base);
     const step_fn fn = d == 128 ? pick_step<128>(g) : pick_step<64>(g);
     prof_begin(K_DECODE_STEP, st);
     hipLaunchKernelGGL(fn, dim3(nsplit, n_kv, B), dim3(ST_THREADS), 0, st, q, k_new, v_new, k_cache, v_cache, past_len,

@@ -83,7 +83,7 @@ int decode_slot_ratio();
 hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                          const int32_t* past_len, int max_past_len, uint16_t* out, float* ws, int B, int n_q,
                          int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
-                         int wg_override, hipStream_t st);
+                         int wg_override, hipStream_t st, float* sched_hdr = nullptr);
 
 // ---- prefill -----------------------------------------------------------------------
 hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -98,10 +98,14 @@ constexpr int DECODE_STEP_MAX_SPLITS = 64;
 // one per tile of the longest context and at most DECODE_STEP_MAX_SPLITS.
 int decode_step_splits(int B, int n_kv, int max_past_len, int window, int n_sink);
 size_t decode_step_workspace_bytes(int B, int n_q, int n_kv, int d);
+// tile bound from which gqa_decode_step runs as rope_append + split-K decode (<= 0: the default)
+void set_decode_step_split_min_tiles(int tiles);
+int decode_step_split_min_tiles();
 hipError_t launch_decode_step(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
                               uint16_t* v_cache, const int32_t* past_len, int max_past_len, uint16_t* out,
-                              uint16_t* q_rot, void* ws, int B, int n_q, int n_kv, int d, int S, const RopeDev& rope,
-                              float scale, int window, int n_sink, const float* sink_logits, hipStream_t st);
+                              uint16_t* q_rot, void* ws, size_t ws_bytes, int B, int n_q, int n_kv, int d, int S,
+                              const RopeDev& rope, float scale, int window, int n_sink, const float* sink_logits,
+                              hipStream_t st);
 
 // ---- decode for wide query groups (g >= 16: both products on MFMA) ------------
 // The decode workspace starts with a header of this many floats (256 bytes)

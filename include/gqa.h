@@ -262,8 +262,8 @@ int gqa_decode_attn_noalloc(const void* q_rot, const void* k_cache, const void* 
                             const gqa_attn_opts* opts, void* stream);
 
 /*
- * gqa_decode_step -- one decode step in a single launch, for small batches:
- * gqa_rope_append (T = 1) followed by gqa_decode_attn, same results.
+ * gqa_decode_step -- one decode step: gqa_rope_append (T = 1) followed by
+ * gqa_decode_attn, same results, in a single launch for small batches.
  *
  * [KV] "RoPE has to know where it is" and "The cache itself is
  * concatenation"; [ATL] "Llama 3 8B - KV cache", cache formula and the
@@ -279,7 +279,10 @@ int gqa_decode_attn_noalloc(const void* q_rot, const void* k_cache, const void* 
  * g >= 16 heads (the threshold of gqa_set_decode_wide_min_group) run instead
  * as gqa_rope_append followed by the wide-group decode kernel, three launches
  * whose matrix-core products beat one launch's vector arithmetic there; the
- * results and the cache writes are the same.
+ * results and the cache writes are the same.  Likewise larger batches (from
+ * 512 tiles of 64 rows, B * n_kv * ceil((max_past_len + 1) / 64), or fewer
+ * under a window; see gqa_set_decode_step_split_min_tiles) run as
+ * gqa_rope_append followed by the split-K decode, the faster path there.
  *
  *   q, k_new, v_new in [B, n_q | n_kv, 1, d] bf16 (q and k unrotated)
  *   k_cache, v_cache in/out [B, n_kv, S, d] bf16; row past_len[b] is written
@@ -287,11 +290,14 @@ int gqa_decode_attn_noalloc(const void* q_rot, const void* k_cache, const void* 
  *   q_rot    out [B, n_q, 1, d] bf16, or NULL (not written)
  *   rope     host pointer, as for gqa_rope_append
  *   scale    <= 0 selects 1/sqrt(d)
- *   workspace  device memory of gqa_decode_step_workspace_bytes(); its first
- *            bytes hold one counter per (sequence, KV head), which must be zero
- *            before the first call (allocate it zero-filled); every call leaves
- *            them zero.  Calls that share a workspace must be stream-ordered,
- *            and it must not be shared with gqa_decode_attn.
+ *   workspace  device memory of at least gqa_decode_step_workspace_bytes(),
+ *            zero-filled before the first call: it starts with one counter per
+ *            (sequence, KV head) and the split-K scheduling header, which every
+ *            call leaves zero; everything else a call writes sits at the end of
+ *            the workspace_bytes given.  So a workspace sized for B sequences
+ *            serves calls of any batch size up to B, through any route, in any
+ *            order.  Calls that share a workspace must be stream-ordered, and it
+ *            must not be shared with gqa_decode_attn.
  * n_q / n_kv must be at most GQA_DECODE_STEP_MAX_GROUP; B and n_kv at most
  * 65535.  Errors: INVALID_ARG, GROUP, HEAD_DIM, RANGE (max_past_len + 1 > S),
  * WORKSPACE, HIP.
@@ -394,6 +400,17 @@ int gqa_set_decode_slot_ratio(int ratio_permille);
  * tolerance.  Returns the value in effect.
  */
 int gqa_set_decode_wide_min_group(int g);
+
+/*
+ * Path override for tests and tuning of gqa_decode_step: the tile bound
+ * (B * n_kv * ceil((max_past_len + 1) / 64), fewer under a window) from which
+ * a step runs as gqa_rope_append followed by the split-K decode instead of
+ * its single-launch kernel.  0 or less restores the default (512); a large
+ * value keeps every step in one launch.  Results agree between the paths
+ * within the attention tolerance (the rotated rows are identical).  Returns
+ * the value in effect.
+ */
+int gqa_set_decode_step_split_min_tiles(int tiles);
 
 #ifdef __cplusplus
 }

@@ -623,7 +623,7 @@ STEP_CASES = [
 ]
 
 
-def run_step(case, seed, ws=None):
+def run_step(case, seed, ws=None, want_q_rot=True):
     B, n_q, n_kv, d, S, past, theta, layout, scaling, rdim, W, NS, learned = case
     q, kn, vn, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed)
     for b in range(B):  # the row being appended: never read before it is written
@@ -635,7 +635,7 @@ def run_step(case, seed, ws=None):
     if poison_unread_tiles((kc, vc, kc_ref, vc_ref), past, W, NS):
         say("  unread window tiles NaN-filled")
     kc_d, vc_d, pl = dev(kc), dev(vc), past_dev(past)
-    q_rot = torch.empty(B, n_q, 1, d, dtype=torch.bfloat16, device=DEV)
+    q_rot = torch.empty(B, n_q, 1, d, dtype=torch.bfloat16, device=DEV) if want_q_rot else None
     out = gq.gqa_decode_step(dev(q), dev(kn), dev(vn), kc_d, vc_d, pl, max(past), theta, layout, scaling, rdim,
                              q_rot=q_rot, workspace=ws, window=W, n_sink=NS,
                              sink_logits=torch.from_numpy(sinks).to(DEV) if learned else None)
@@ -658,6 +658,57 @@ def test_decode_step_parity(case):
         other[past[b]] = False
         assert np.array_equal(kc_g[b][:, other], kc_in[b][:, other])
         assert max_ulp(kc_g[b][:, past[b]], kc_ref[b][:, past[b]]) <= 1
+
+
+LARGE_STEP_CASES = [
+    # tile bounds 8 x 8 x 32 = 2048 and 6 x 8 x 18 = 864 (window): past the split threshold of 512
+    (8, 32, 8, 128, 2048, [2047, 0, 63, 64, 1000, 1500, 777, 2046], 5.0e5, "interleaved", SCALED, None, 0, 0, True),
+    (6, 32, 8, 128, 3000, [2999, 10, 1500, 64, 2500, 999], 5.0e5, "half", None, None, 1000, 4, True),
+]
+
+
+@pytest.mark.parametrize("route", ["split", "single"])
+@pytest.mark.parametrize("case", LARGE_STEP_CASES, ids=lambda c: f"B{c[0]}W{c[10]}")
+def test_decode_step_large_batch_routes(case, route):
+    """Batches past the tile threshold: by default the step runs as rope_append + split-K decode; with the
+    threshold raised it stays one launch.  Both against the oracle doing its own RoPE and append."""
+    say(f"decode_step large batch, route {route}, {case[:6]}")
+    B, S, past = case[0], case[4], case[5]
+    gq.gqa_set_decode_step_split_min_tiles(0 if route == "split" else 1 << 30)
+    try:
+        out, ref, (q_rot, q_ref, kc_d, kc_ref, vc_d, vc_ref, kc_in) = run_step(case, seed=2100 + B)
+    finally:
+        gq.gqa_set_decode_step_split_min_tiles(0)
+    check_out(synth.bits(out), ref, f"decode_step {route}")
+    assert max_ulp(synth.bits(q_rot), q_ref) <= 1
+    assert np.array_equal(synth.bits(vc_d), vc_ref), "value row appended bit for bit, nothing else touched"
+    kc_g = synth.bits(kc_d)
+    for b in range(B):
+        other = np.ones(S, dtype=bool)
+        other[past[b]] = False
+        assert np.array_equal(kc_g[b][:, other], kc_in[b][:, other])
+        assert max_ulp(kc_g[b][:, past[b]], kc_ref[b][:, past[b]]) <= 1
+
+
+def test_decode_step_workspace_serves_every_batch_size_and_route():
+    """One workspace sized for the largest batch serves steps of several batch sizes through all routes in
+    turn (split-K, single launch, forced either way; the rotated q returned or kept in the workspace); every
+    call matches the oracle and leaves the first 256 bytes (single-launch counters, split-K ticket) zero."""
+    n_q, n_kv, d, S = 32, 8, 128, 1200
+    rng = np.random.default_rng(41)
+    ws = torch.zeros(gq.gqa_decode_step_workspace_bytes(16, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    plan = [(16, 0), (2, 0), (16, 1 << 30), (8, 0), (2, 1), (16, 0), (8, 1 << 30)]
+    try:
+        for i, (B, thr) in enumerate(plan):
+            past = [int(x) for x in rng.integers(0, S - 1, size=B)]
+            case = (B, n_q, n_kv, d, S, past, 5.0e5, "interleaved", None, None, 0, 0, False)
+            gq.gqa_set_decode_step_split_min_tiles(thr)
+            say(f"  call {i}: B{B} threshold {gq.gqa_set_decode_step_split_min_tiles(thr)}")
+            out, ref, _ = run_step(case, seed=2200 + i, ws=ws, want_q_rot=(i % 2 == 0))
+            check_out(synth.bits(out), ref, f"decode_step call {i} B{B}")
+            assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "first 256 bytes must be zero after a call"
+    finally:
+        gq.gqa_set_decode_step_split_min_tiles(0)
 
 
 def test_decode_step_repeat_calls_and_workspace_reuse():
