@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -17,6 +18,33 @@
 // this name is only a stand-in for the symbol; the device address of each
 // GPU's copy comes from hipGetSymbolAddress (decode_scratch_ptr below).
 static __device__ __align__(256) unsigned char scratch[GQA_DECODE_NOALLOC_MAX_BYTES];
+
+namespace gqa {
+
+hipError_t device_cu_count(int* n) {
+    constexpr int MAX_DEVICES = 64;
+    static std::atomic<int> cache[MAX_DEVICES] = {};  // 0: not looked up yet
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < MAX_DEVICES;
+    if (cached) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *n = c;
+            return hipSuccess;
+        }
+    }
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (c < 1) c = 1;
+    if (cached) cache[dev].store(c, std::memory_order_relaxed);
+    *n = c;
+    return hipSuccess;
+}
+
+}  // namespace gqa
 
 namespace {
 

@@ -1004,12 +1004,9 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
     const DecodePlan p = decode_plan(n_q, n_kv, d);
     const Variant& v = pick_variant(n_q / n_kv);
 
-    static int cu_count = 0;
-    if (cu_count == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    int cu_count = 0;
+    {
+        const hipError_t e = device_cu_count(&cu_count);
         if (e != hipSuccess) return e;
     }
     int G = wg_override;

@@ -391,13 +391,8 @@ size_t step_counter_bytes(int B, int n_kv) {
 }  // namespace
 
 int decode_step_splits(int B, int n_kv, int max_past_len, int window, int n_sink) {
-    static int cu_count = 0;
-    if (cu_count == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cu_count = 256;
-    }
+    int cu_count = 256;  // (the launch itself reports a device error)
+    if (device_cu_count(&cu_count) != hipSuccess) cu_count = 256;
     long long tiles = (max_past_len + 1 + 63) / 64;
     if (window > 0) {
         const long long wt = (n_sink + 63) / 64 + window / 64 + 2;

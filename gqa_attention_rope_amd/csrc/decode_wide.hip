@@ -431,13 +431,8 @@ using wide_fn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, cons
 constexpr int WD_MAX_SEG_RECORDS = 2048;
 
 int decode_wide_splits(int nb, int n_kv, int g, int max_past_len, int window, int n_sink, int wg_override) {
-    static int cu_count = 0;
-    if (cu_count == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cu_count = 256;
-    }
+    int cu_count = 256;  // (the launch itself reports a device error)
+    if (device_cu_count(&cu_count) != hipSuccess) cu_count = 256;
     long long tiles = (max_past_len + 1 + 63) / 64;
     if (window > 0) {
         const long long wt = (n_sink + 63) / 64 + window / 64 + 2;

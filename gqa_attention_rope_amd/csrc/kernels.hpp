@@ -85,6 +85,10 @@ hipError_t launch_decode(const uint16_t* q_rot, const uint16_t* k_cache, const u
                          int n_kv, int d, int S, float scale, int window, int n_sink, const float* sink_logits,
                          int wg_override, hipStream_t st, float* sched_hdr = nullptr);
 
+// Compute units of the current device, looked up once per device (launch
+// shapes are sized from it).
+hipError_t device_cu_count(int* n);
+
 // ---- prefill -----------------------------------------------------------------------
 hipError_t launch_prefill(const uint16_t* q_rot, const uint16_t* k_cache, const uint16_t* v_cache,
                           const int32_t* past_len, int max_past_len, uint16_t* out, int B, int n_q, int n_kv, int T,
