@@ -488,8 +488,11 @@ def main():
     value = kv_step / (ms * 1e-3) / 1e9
     tok_s = info["B"] / (ms * 1e-3)
 
-    # decode attention alone: the 32 layers' gqa_decode_attn calls (partials + combine) back to back
-    attn_layers_ms, _ = timed(info["attention_only"], args.steps, args.warmup, stream)
+    # decode attention alone: the 32 layers' gqa_decode_attn calls (partials + combine) back to back, timed
+    # over at least 50 loops after at least 10 warm-up loops whatever --steps is (a secondary figure: a short
+    # loop right after the step loop measured 1-3 % slow)
+    attn_reps, attn_warm = max(args.steps, 50), max(args.warmup, 10)
+    attn_layers_ms, _ = timed(info["attention_only"], attn_reps, attn_warm, stream)
     attn_ms = attn_layers_ms / info["layers"]
     avg_ms, per_kind = kernel_avg(gq, step, max(5, args.steps // 5), "decode_partial")
     comb_ms = per_kind["decode_combine"][0] / max(per_kind["decode_combine"][1], 1)
@@ -505,8 +508,8 @@ def main():
                 "traffic_over_alg": round(t_attn / alg, 4) if t_attn else None,
                 "kernel": "decode attention per layer: decode_partial_kernel<128,4,1> + decode_combine_kernel<128>",
                 "avg_launch_us": round(attn_ms * 1e3, 2), "alg_bytes_per_launch": alg,
-                "timing": f"HIP events around {args.steps} x 32 back-to-back gqa_decode_attn calls (two kernels "
-                          f"each), per call",
+                "timing": f"HIP events around {attn_reps} x 32 back-to-back gqa_decode_attn calls (two kernels "
+                          f"each, after {attn_warm} x 32 untimed), per call",
                 "dominant_kernel": {"kernel": "decode_partial_kernel<128,4,1>", "achieved": round(achieved_p, 1),
                                     "frac": round(achieved_p / HBM_PEAK_GBS, 4), "avg_launch_us": round(avg_ms * 1e3, 2),
                                     "traffic": t_part,
