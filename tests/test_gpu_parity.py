@@ -359,6 +359,26 @@ def test_decode_workspace_reuse_leaves_header_zero():
         assert int(ws[:256].count_nonzero()) == 0, "scheduling header must be zero after a call"
 
 
+def test_decode_workspace_serves_smaller_batches():
+    """A decode workspace sized for six sequences serves calls of 6, 2, 5, 1 and 6 sequences in turn (the
+    scheduling header sits at a fixed place and is zero after every call; the record directory and the
+    records are rewritten by each call), each matching the oracle."""
+    n_q, n_kv, d, S = 32, 8, 128, 3000
+    ws = torch.zeros(gq.gqa_decode_workspace_bytes(6, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(43)
+    for it, B in enumerate((6, 2, 5, 1, 6)):
+        past = [int(x) for x in rng.integers(0, S - 1, size=B)]
+        q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=2300 + it)
+        for b in range(B):  # row past_len is attended here: make it finite
+            kc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 2400 + 10 * it + b))
+            vc[b, :, past[b]] = synth.bits(synth.normal_bf16((n_kv, d), 2500 + 10 * it + b))
+        ref = attend(q, kc, vc, past, n_kv)
+        out = gq.gqa_decode_attn(dev(q), dev(kc), dev(vc), past_dev(past), max(past), workspace=ws)
+        torch.cuda.synchronize()
+        check_out(synth.bits(out), ref, f"decode B{B} on a six-sequence workspace")
+        assert int(ws[:256].count_nonzero()) == 0, "scheduling header must be zero after a call"
+
+
 def test_decode_scale_argument():
     B, n_q, n_kv, d, S, past = 2, 8, 2, 128, 128, [100, 20]
     q, _, _, kc, vc = make_inputs(B, n_q, n_kv, 1, d, S, past, seed=8)
