@@ -543,6 +543,9 @@ def main():
         "tokens_per_s": round(tok_s, 1),
         "wall_s_timed": round(wall, 3),
         "kernels": kinds,
+        "kernels_timing": "HIP events on the launch stream around each launch, mean per launch; each bracket also "
+                          "holds that launch's dispatch gap, so the kinds sum to more than ms_per_step / layers "
+                          "(the rocprofv3 kernel durations under profiles/ do not)",
         "decode_attention": decode_attention,
         "roofline": roofline,
     }
