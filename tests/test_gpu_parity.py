@@ -710,6 +710,20 @@ def test_decode_step_large_batch_routes(case, route):
         assert max_ulp(kc_g[b][:, past[b]], kc_ref[b][:, past[b]]) <= 1
 
 
+def test_decode_step_split_route_repeatable():
+    """The split route of the step (rope_append + split-K) gives bitwise identical results on a reused
+    workspace and leaves its first 256 bytes zero."""
+    case = LARGE_STEP_CASES[0]
+    B, n_q, n_kv, d, S = case[0], case[1], case[2], case[3], case[4]
+    ws = torch.zeros(gq.gqa_decode_step_workspace_bytes(B, n_q, n_kv, d, S), dtype=torch.uint8, device=DEV)
+    out1, ref, _ = run_step(case, seed=2150, ws=ws, want_q_rot=False)
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    out2, _, _ = run_step(case, seed=2150, ws=ws, want_q_rot=False)
+    assert torch.equal(out1, out2), "repeated split-route step differs"
+    check_out(synth.bits(out2), ref, "decode_step split route, second call")
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+
+
 def test_decode_step_workspace_serves_every_batch_size_and_route():
     """One workspace sized for the largest batch serves steps of several batch sizes through all routes in
     turn (split-K, single launch, forced either way; the rotated q returned or kept in the workspace); every
