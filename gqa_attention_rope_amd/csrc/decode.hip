@@ -369,10 +369,13 @@ __global__ __launch_bounds__(THREADS, 2) void decode_partial_kernel(
     // Record directory for the combine: for segment s, the slot of its first
     // static piece and their count, the slot of its first chunk piece and
     // their count, the first static workgroup and the static tile total.
-    // Workgroup w fills the entries of segments w + G k (one per thread).  The
-    // stores go out before the first tile loads, so the waits for those loads
-    // keep their fixed counts.
-    for (int s = w + G * tid; s < n_segs; s += G * THREADS) {
+    // The last workgroups of the grid fill it, one segment per thread (the
+    // last one segments 0 .. 255, the one before it the next 256, ...): each
+    // entry costs two owner searches, about 0.85 us of one wave, which would
+    // otherwise delay the first loads of the first-slot workgroups, the ones
+    // with the larger shares.  The stores go out before the first tile loads,
+    // so the waits for those loads keep their fixed counts.
+    for (int s = (G - 1 - w) * THREADS + tid; s < n_segs; s += G * THREADS) {
         const int b = s / segs_per_b, sj = s - b * segs_per_b;
         const int nt = s_pre[b + 1] - s_pre[b];
         const long long start = (long long)segs_per_b * s_pre[b] + (long long)sj * nt;
